@@ -1,0 +1,98 @@
+"""Seeded synthetic inputs for Dual Chunk Attention workloads.
+
+This module holds no arithmetic of the method: it only draws inputs and rounds them to bf16.  Both
+the GPU path (tests, benchmark) and the CPU oracle read the bytes it produces.
+
+Recipe: numpy ``default_rng(seed)``; draw Q, then K, then freq_factors; Q and K are i.i.d.
+standard normal float32 (unit RMS, as after q/k-norm), rounded to bf16 by round-to-nearest-even
+for bf16 workloads; freq_factors are float32 uniform in [1, 8) (all 1.0 for the fp32 workload).
+Keys are cache cells 0..N-1 at positions equal to their index; prefill queries are the positions
+listed per workload; decode queries sit at N-1.
+"""
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    T: int
+    q0: int            # first query position; query t of every sequence sits at q0 + t
+    N: int             # KV cache length per sequence
+    chunk: int
+    Hq: int
+    Hkv: int
+    dtype: str         # "f32" or "bf16"
+    seed: int
+    D: int = 512
+    n_rot: int = 128
+    theta: float = 1.0e6
+    ff_uniform: bool = True   # freq_factors ~ U[1,8); False -> all 1.0
+    notes: str = field(default="", compare=False)
+
+    @property
+    def scale(self) -> float:
+        return float(1.0 / np.sqrt(self.D))
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("prefill-256-c64-fp32", 1, 256, 0, 256, 64, 2, 1, "f32", 1, ff_uniform=False,
+                 notes="tiny single global layer, fp32, all three regimes"),
+        Workload("prefill-4k-c1024", 1, 4096, 0, 4096, 1024, 16, 2, "bf16", 2),
+        Workload("prefill-32k-c8192", 1, 32768, 0, 32768, 8192, 16, 2, "bf16", 3),
+        Workload("decode-b8-kv256k-c65536", 8, 1, 262143, 262144, 65536, 16, 2, "bf16", 4),
+        Workload("prefill-4k-at-1m-c65536", 1, 4096, 1044480, 1048576, 65536, 16, 2, "bf16", 5),
+    ]
+}
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bf16 (nearest-even) and return the uint16 bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact float32 value of bf16 bit patterns."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _normal(rng, shape, as_bf16, chunk_elems=1 << 24):
+    """Standard normal float32 of `shape`, drawn in chunks (same stream as one draw)."""
+    n = int(np.prod(shape))
+    out = np.empty(n, np.uint16 if as_bf16 else np.float32)
+    for s in range(0, n, chunk_elems):
+        e = min(n, s + chunk_elems)
+        v = rng.standard_normal(e - s, dtype=np.float32)
+        out[s:e] = bf16_bits(v) if as_bf16 else v
+    return out.reshape(shape)
+
+
+def make_inputs(w, *, B=None, T=None, q0=None, N=None, seed=None):
+    """Inputs of workload `w` (a Workload or its name); size overrides give smaller cases of the
+    same recipe.  Returns dict(q, k, q_pos, freq_factors, w): q [B,T,Hq,D], k [B,N,Hkv,D] as
+    uint16 bf16 bits (bf16 workloads) or float32; q_pos int32 [B,T]; freq_factors float32
+    [n_rot/2]."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    B = w.B if B is None else B
+    T = w.T if T is None else T
+    q0 = w.q0 if q0 is None else q0
+    N = w.N if N is None else N
+    seed = w.seed if seed is None else seed
+    rng = np.random.default_rng(seed)
+    as_bf16 = w.dtype == "bf16"
+    q = _normal(rng, (B, T, w.Hq, w.D), as_bf16)
+    k = _normal(rng, (B, N, w.Hkv, w.D), as_bf16)
+    if w.ff_uniform:
+        ff = rng.uniform(1.0, 8.0, w.n_rot // 2).astype(np.float32)
+    else:
+        ff = np.ones(w.n_rot // 2, np.float32)
+    q_pos = (q0 + np.arange(T, dtype=np.int64)).astype(np.int32)
+    q_pos = np.ascontiguousarray(np.broadcast_to(q_pos, (B, T)))
+    return dict(q=q, k=k, q_pos=q_pos, freq_factors=ff, w=w)

@@ -1,0 +1,151 @@
+"""CPU oracle for Dual Chunk Attention: thin ctypes wrapper over the fp64 C code in dca_oracle.c.
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, the smoke check and the benchmark's CPU-baseline leg may
+import this package; the GPU library neither imports nor links it, and it imports nothing from
+the GPU library.  Every function below states the passage of the pages it follows (see the header
+of dca_oracle.c for the remap and RoPE readings it fixes).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+INTRA, SUCC, INTER = 0, 1, 2
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        path = _build.LIB
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+            _build.build()
+        lib = ctypes.CDLL(path)
+        i64, i32p, f64p = ctypes.c_int64, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)
+        lib.dca_oracle_regime.restype = ctypes.c_int
+        lib.dca_oracle_regime.argtypes = [i64, i64, i64, i64]
+        lib.dca_oracle_query_pos.restype = i64
+        lib.dca_oracle_query_pos.argtypes = [i64, i64, ctypes.c_int]
+        lib.dca_oracle_key_pos.restype = i64
+        lib.dca_oracle_key_pos.argtypes = [i64, i64]
+        lib.dca_oracle_remap.restype = i64
+        lib.dca_oracle_remap.argtypes = [i64, i64, i32p, i64, i32p, i32p, i32p, ctypes.c_int]
+        lib.dca_oracle_rope.restype = None
+        lib.dca_oracle_rope.argtypes = [i64, i64, ctypes.c_double, f64p, f64p,
+                                        ctypes.POINTER(ctypes.c_int64), i64, i64, f64p]
+        lib.dca_oracle_merge.restype = None
+        lib.dca_oracle_merge.argtypes = [i64, f64p, f64p, i64, i64, f64p, f64p]
+        lib.dca_oracle_attention.restype = ctypes.c_int
+        lib.dca_oracle_attention.argtypes = [
+            i64, i64, i64, i64, i64, ctypes.c_double, ctypes.c_double, f64p, ctypes.c_int,
+            i64, i64, ctypes.c_void_p, i32p, ctypes.c_void_p, i64, i64,
+            ctypes.POINTER(ctypes.c_int64), f64p, f64p, f64p, f64p, ctypes.c_int]
+        _LIB = lib
+    return _LIB
+
+
+def _ptr(a, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def regime(i, j, c, n_kv):
+    """Regime of key j for a query at i (DCA feature page, "Section C design" table, read as in
+    the header of dca_oracle.c); -1 when the key is not attended."""
+    return _lib().dca_oracle_regime(int(i), int(j), int(c), int(n_kv))
+
+
+def query_pos(i, c, r):
+    """Remapped query position of regime r (intra i mod c, succ (i mod c)+c, inter c-1)."""
+    return _lib().dca_oracle_query_pos(int(i), int(c), int(r))
+
+
+def key_pos(j, c):
+    """Key position j mod c (rope-K-once, "Section C design")."""
+    return _lib().dca_oracle_key_pos(int(j), int(c))
+
+
+def remap(c, qpos, n_kv, n_threads=0):
+    """Positions and per-regime key intervals by enumeration of the explicit predicate.
+
+    Returns (pos_q int32 [3, rows], pos_k int32 [n_kv], bounds int32 [3, rows, 2], status);
+    status 0 means every regime key set was one contiguous interval."""
+    qpos = np.ascontiguousarray(np.asarray(qpos, dtype=np.int32).reshape(-1))
+    rows = qpos.size
+    pos_q = np.zeros((3, rows), np.int32)
+    pos_k = np.zeros((max(n_kv, 0),), np.int32)
+    bounds = np.zeros((3, rows, 2), np.int32)
+    st = _lib().dca_oracle_remap(int(c), rows, _ptr(qpos, ctypes.c_int32), int(n_kv),
+                                 _ptr(pos_q, ctypes.c_int32), _ptr(pos_k, ctypes.c_int32),
+                                 _ptr(bounds, ctypes.c_int32), int(n_threads))
+    return pos_q, pos_k, bounds, int(st)
+
+
+def rope(x, pos, n_rot, theta, freq_factors=None):
+    """Partial RoPE of x [rows, H, D] (fp64) at integer positions pos [rows] ("DCA algorithm":
+    only the rotary dims move; proportional rope with freq_factors, "Why llamafile is
+    sufficient")."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    rows, H, D = x.shape
+    pos = np.ascontiguousarray(np.asarray(pos, dtype=np.int64).reshape(rows))
+    y = np.empty_like(x)
+    ff = None if freq_factors is None else np.ascontiguousarray(freq_factors, dtype=np.float64)
+    _lib().dca_oracle_rope(int(n_rot), D, float(theta), None if ff is None else _ptr(ff, ctypes.c_double),
+                           _ptr(x, ctypes.c_double), _ptr(pos, ctypes.c_int64), rows, H,
+                           _ptr(y, ctypes.c_double))
+    return y
+
+
+def merge(o_parts, lse_parts):
+    """N-way LSE merge (Implementation progress + Section-D simplification).
+    o_parts [P, rows, D], lse_parts [P, rows] -> (o [rows, D], lse [rows])."""
+    o_parts = np.ascontiguousarray(o_parts, dtype=np.float64)
+    lse_parts = np.ascontiguousarray(lse_parts, dtype=np.float64)
+    P, rows, D = o_parts.shape
+    o = np.empty((rows, D), np.float64)
+    lse = np.empty((rows,), np.float64)
+    _lib().dca_oracle_merge(P, _ptr(o_parts, ctypes.c_double), _ptr(lse_parts, ctypes.c_double),
+                            rows, D, _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double))
+    return o, lse
+
+
+def attention(q, qpos, k, *, chunk, n_rot, theta, scale, freq_factors=None, rows=None,
+              per_regime=True, n_threads=0):
+    """DCA attention of selected query rows in fp64.
+
+    q [B, T, Hq, D] and k [B, N, Hkv, D] are float32 arrays or uint16 bf16 bit patterns (same
+    kind for both); qpos int32 [B, T]; rows = flat row indices b*T+t (default: all).
+    Returns dict(o [n, Hq, D], lse [n, Hq], o_reg [3, n, Hq, D], lse_reg [3, n, Hq], rows)."""
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    if q.dtype == np.uint16 and k.dtype == np.uint16:
+        in_bf16 = 1
+    elif q.dtype == np.float32 and k.dtype == np.float32:
+        in_bf16 = 0
+    else:
+        raise TypeError("q and k must both be float32 or both uint16 (bf16 bits)")
+    B, T, Hq, D = q.shape
+    Bk, N, Hkv, Dk = k.shape
+    assert Bk == B and Dk == D
+    qpos = np.ascontiguousarray(np.asarray(qpos, dtype=np.int32).reshape(B, T))
+    sel = np.arange(B * T, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    n = sel.size
+    o = np.zeros((n, Hq, D), np.float64)
+    lse = np.zeros((n, Hq), np.float64)
+    o_reg = np.zeros((3, n, Hq, D), np.float64) if per_regime else None
+    lse_reg = np.zeros((3, n, Hq), np.float64) if per_regime else None
+    ff = None if freq_factors is None else np.ascontiguousarray(freq_factors, dtype=np.float64)
+    st = _lib().dca_oracle_attention(
+        D, int(n_rot), Hq, Hkv, int(chunk), float(theta), float(scale),
+        None if ff is None else _ptr(ff, ctypes.c_double), in_bf16, B, T,
+        q.ctypes.data_as(ctypes.c_void_p), _ptr(qpos, ctypes.c_int32),
+        k.ctypes.data_as(ctypes.c_void_p), N, n, _ptr(sel, ctypes.c_int64),
+        _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double),
+        None if o_reg is None else _ptr(o_reg, ctypes.c_double),
+        None if lse_reg is None else _ptr(lse_reg, ctypes.c_double), int(n_threads))
+    if st != 0:
+        raise RuntimeError(f"oracle attention failed with status {st}")
+    return dict(o=o, lse=lse, o_reg=o_reg, lse_reg=lse_reg, rows=sel)
