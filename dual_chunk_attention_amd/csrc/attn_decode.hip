@@ -1,0 +1,247 @@
+// Split-KV regime passes for bf16 decode (few query tokens per sequence) on gfx950.
+//
+// Same math as the prefill passes (DCA feature page, "DCA algorithm", "Implementation progress
+// + Section-D simplification", "Section C2b"): per query row and regime, softmax over the
+// regime's key interval with the regime-rotated query, values = raw keys, normalised O and
+// natural-log lse, (0, -inf) when empty.  Decode is bound by reading the cache, so:
+//  * Keys are read exactly once: the rotary dims are rotated in registers at j mod c from
+//    cos/sin tables formed in fp64 (lo[p & 63][f] composed with hi[p >> 6][f] by the angle
+//    addition formulas) instead of being read from a pre-rotated copy.  (When the caller passes
+//    pre-rotated keys instead, those are read.)
+//  * The cache of one (sequence, KV head) is split into spans of `span` keys; each workgroup
+//    handles one (query row, KV head, span) and writes one partial per regime that meets its
+//    span; the partials are merged by the N-way LSE merge.  A regime that misses the span
+//    writes lse = -inf only.
+//  * 4 waves cooperate on 64-key tiles staged by direct global->LDS loads (double buffered):
+//    wave w computes S^T = K Q^T for keys [16w, 16w+16) with MFMA 16x16x32 (the G query heads of
+//    the KV head are the 16 columns, padded), the per-head maximum is exchanged through LDS,
+//    P goes to LDS as bf16, and wave w computes O^T = V^T P^T for head dims [128w, 128w+128)
+//    with V^T fragments from the LDS transpose read.
+#include "common.h"
+
+namespace dca {
+namespace {
+
+constexpr int kD = 512;
+constexpr int kTile = 64;
+constexpr int kTileBytes = kTile * kD * 2;   // 64 KiB
+constexpr float kTau = 8.0f;
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+template <bool ROTATE>
+__global__ __launch_bounds__(256, 1) void attn_decode_kernel(DecodeArgs da) {
+  const AttnArgs& a = da.base;
+  __shared__ __attribute__((aligned(1024))) char kbuf[2 * kTileBytes];
+  __shared__ __attribute__((aligned(16))) bf16 pbuf[16 * kTile];     // P[head][key]
+  __shared__ float smax[4][16], ssum[4][16];
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int hcol = l & 15, gq = l >> 4;   // column (query head) and 16-lane group
+  const int G = a.Hq / a.Hkv;
+  const int64_t rows = (int64_t)a.B * a.T;
+  const int span = blockIdx.x;
+  const int64_t btg = blockIdx.y;
+  const int g = (int)(btg % a.Hkv);
+  const int64_t bt = btg / a.Hkv;
+  const int b = (int)(bt / a.T);
+  const int span_lo = span * da.span;
+  const int span_hi = min(span_lo + da.span, a.n_kv) - 1;
+  const bool head_ok = hcol < G;
+  const int64_t rowhead = bt * a.Hq + (int64_t)g * G + (head_ok ? hcol : 0);
+
+  const bf16* kraw_b = (const bf16*)a.k_raw + ((int64_t)b * a.n_kv * a.Hkv + g) * kD;
+  const bf16* krot_b =
+      ROTATE ? nullptr : (const bf16*)a.k_rot + ((int64_t)b * a.n_kv * a.Hkv + g) * a.k_rot_hs;
+  const int half_rot = a.n_rot / 2;   // 64
+  const float scale_log2 = a.scale * kLog2e;
+
+  // query fragments: B operand lane l holds Q[head hcol][32 s + 8 gq .. +7]
+  bf16x8 q[16];
+  {
+    const bf16* qt = (const bf16*)a.q_tail + rowhead * a.q_tail_hs + 8 * gq;
+#pragma unroll
+    for (int s = 4; s < 16; ++s) {
+      bf16x8 v = *(const bf16x8*)(qt + 32 * s - 128);
+      q[s] = head_ok ? v : bf16x8{};
+    }
+  }
+  // LDS offsets.  QK operand: key row 16w + hcol, chunk 4s + gq.
+  const int qrow = 16 * w + hcol;
+  int qk_off[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) qk_off[u] = qrow * 1024 + 16 * ((4 * u + gq) ^ swz(qrow & 7));
+  // PV operand (transpose read): rows 32 ks + 8 gq + 4 e + j/4, dims 128 w + 16 dt + 4 (j%4).
+  const int j16 = l & 15;
+
+  for (int r = 0; r < 3; ++r) {
+    if (!(da.regime_mask & (1 << r))) continue;
+    const int slot = da.slot0[r] + span;
+    float* lse_out = da.lse_part + (int64_t)slot * rows * a.Hq;
+    const int lo_r = max(a.bounds[(r * rows + bt) * 2 + 0], 0);
+    const int hi_r = min(a.bounds[(r * rows + bt) * 2 + 1], a.n_kv - 1);
+    const int lo = max(lo_r, span_lo), hi = min(hi_r, span_hi);
+    if (lo > hi) {
+      if (tid < G) lse_out[bt * a.Hq + (int64_t)g * G + tid] = -INFINITY;
+      continue;
+    }
+    {
+      const bf16* qr = (const bf16*)a.q_rot[r] + rowhead * a.q_rot_hs + 8 * gq;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bf16x8 v = *(const bf16x8*)(qr + 32 * s);
+        q[s] = head_ok ? v : bf16x8{};
+      }
+    }
+    f32x4 o[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{};
+    float m_used = -INFINITY, l_part = 0.0f;
+
+    const int kt0 = lo / kTile, kt1 = hi / kTile;
+    auto issue = [&](int buf, int k0) {
+      char* base = kbuf + buf * kTileBytes;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 16 * w + i;
+        int key = k0 + row;
+        key = key < a.n_kv ? key : a.n_kv - 1;
+        const int c = l ^ swz(row & 7);
+        __builtin_amdgcn_global_load_lds(kraw_b + (int64_t)key * a.Hkv * kD + 8 * c,
+                                         (lds_void*)(base + row * 1024), 16, 0, 0);
+      }
+    };
+    issue(0, kt0 * kTile);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    for (int kt = kt0; kt <= kt1; ++kt) {
+      const int cur = (kt - kt0) & 1;
+      const int k0 = kt * kTile;
+      if (kt < kt1) issue(cur ^ 1, k0 + kTile);
+      const char* kb = kbuf + cur * kTileBytes;
+      const int key = k0 + qrow;
+
+      // ---- S^T for keys [16w, 16w+16) --------------------------------------------------
+      bf16x8 kf[16];
+#pragma unroll
+      for (int s = 0; s < 16; ++s) kf[s] = *(const bf16x8*)(kb + qk_off[s & 3] + 256 * (s >> 2));
+      if (ROTATE) {
+        const int64_t pos = (int64_t)min(key, a.n_kv - 1) % da.chunk;
+        const float2* tlo = da.rot_lo + (pos & 63) * half_rot;
+        const float2* thi = da.rot_hi + (pos >> 6) * half_rot;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int f = 32 * s + 8 * gq + e;
+            const float2 A = tlo[f], Bv = thi[f];
+            const float cs = A.x * Bv.x - A.y * Bv.y;
+            const float sn = A.y * Bv.x + A.x * Bv.y;
+            const float x0 = (float)kf[s][e], x1 = (float)kf[s + 2][e];
+            kf[s][e] = (bf16)fmaf(x0, cs, -x1 * sn);
+            kf[s + 2][e] = (bf16)fmaf(x0, sn, x1 * cs);
+          }
+        }
+      } else {
+        const bf16* kr = krot_b + (int64_t)min(key, a.n_kv - 1) * a.Hkv * a.k_rot_hs + 8 * gq;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) kf[s] = *(const bf16x8*)(kr + 32 * s);
+      }
+      f32x4 sacc = f32x4{};
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], q[s], sacc, 0, 0, 0);
+      // C layout: reg e = key 16w + 4 gq + e, column = head hcol
+      float sv[4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int kk = k0 + 16 * w + 4 * gq + e;
+        sv[e] = (kk < lo || kk > hi) ? -INFINITY : sacc[e] * scale_log2;
+        mx = fmaxf(mx, sv[e]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      if (gq == 0) smax[w][hcol] = mx;
+      __syncthreads();
+      const float tmax = fmaxf(fmaxf(smax[0][hcol], smax[1][hcol]), fmaxf(smax[2][hcol], smax[3][hcol]));
+      const bool need = tmax > m_used + kTau;
+      if (__ballot(need)) {
+        const float m_new = need ? tmax : m_used;
+        const float alpha = exp2f(m_used - m_new);
+        l_part *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+        m_used = m_new;
+      }
+      bf16x4 pv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = sv[e] == -INFINITY ? 0.0f : exp2f(sv[e] - m_used);
+        l_part += p;
+        pv[e] = (bf16)p;
+      }
+      *(bf16x4*)(pbuf + hcol * kTile + 16 * w + 4 * gq) = pv;
+      __syncthreads();
+
+      // ---- O^T += V^T P^T for dims [128w, 128w+128) --------------------------------------
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 pb = *(const bf16x8*)(pbuf + hcol * kTile + 32 * ks + 8 * gq);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          bf16x4 v[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int row = 32 * ks + 8 * gq + 4 * e + (j16 >> 2);
+            const int c = 16 * w + 2 * dt + ((j16 >> 1) & 1);
+            const int off = row * 1024 + 16 * (c ^ swz(row & 7)) + 8 * (j16 & 1);
+            v[e] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(kb + off));
+          }
+          bf16x8 vf;
+          vf[0] = v[0][0]; vf[1] = v[0][1]; vf[2] = v[0][2]; vf[3] = v[0][3];
+          vf[4] = v[1][0]; vf[5] = v[1][1]; vf[6] = v[1][2]; vf[7] = v[1][3];
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb, o[dt], 0, 0, 0);
+        }
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+
+    // ---- combine the row sums of the 4 waves and store the partial ----------------------------
+    float ls = l_part;
+    ls += __shfl_xor(ls, 16, 64);
+    ls += __shfl_xor(ls, 32, 64);
+    if (gq == 0) ssum[w][hcol] = ls;
+    __syncthreads();
+    const float l_tot = (ssum[0][hcol] + ssum[1][hcol]) + (ssum[2][hcol] + ssum[3][hcol]);
+    const bool nonempty = l_tot > 0.0f;
+    const float inv = nonempty ? 1.0f / l_tot : 0.0f;
+    if (head_ok) {
+      float* orow = da.o_part + ((int64_t)slot * rows * a.Hq + rowhead) * kD + 128 * w + 4 * gq;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) *(f32x4*)(orow + 16 * dt) = o[dt] * inv;
+      if (gq == 0 && w == 0) lse_out[rowhead] = nonempty ? (m_used + log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.base.B * a.base.T;
+  if (rows <= 0 || a.n_spans <= 0) return hipSuccess;
+  dim3 grid((unsigned)a.n_spans, (unsigned)(rows * a.base.Hkv)), block(256);
+  if (a.rot_lo)
+    hipLaunchKernelGGL(attn_decode_kernel<true>, grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(attn_decode_kernel<false>, grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace dca

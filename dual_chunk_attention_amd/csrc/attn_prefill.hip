@@ -1,0 +1,301 @@
+// Regime flash-attention passes for bf16 prefill on gfx950 (MFMA 32x32x16 bf16).
+//
+// What it computes (DCA feature page, "DCA algorithm" and "Implementation progress +
+// Section-D simplification"): for every query row and each requested regime r, the softmax
+// attention over that row's regime key interval [lo, hi] with scores
+//   s = scale * (<q_r[0:128], k_rot[0:128]> + <q[128:512], k[128:512]>)
+// (q_r rotated at the regime position, k_rot rotated at j mod c) and values v = k (raw, K = V),
+// written as normalised O_r (fp32) and lse_r = m + ln(sum e^(s-m)); an empty interval gives
+// O_r = 0, lse_r = -inf ("Section C2b"; Upstream Sync entry 0110).
+//
+// Work decomposition (one workgroup of 4 waves per (sequence b, KV head g, query block)):
+//  * The 128 rows of a workgroup are QB = 128/G query positions x the G query heads that share
+//    KV head g (GQA), so every K tile staged in LDS serves all of them.  Wave w owns rows
+//    [32w, 32w+32); lane l owns row l%32 in both halves of the wave.
+//  * Scores are computed transposed, S^T = K Q^T: K is the MFMA A operand (read from LDS),
+//    Q^T the B operand (kept in 128 VGPRs for the whole pass).  In the 32x32 result layout a
+//    lane holds 16 keys of its own row, so the row max/sum needs one cross-half exchange.
+//  * O^T = V^T P^T: the score registers, converted to bf16, are already the B operand (the key
+//    order inside the MFMA k-slots is permuted identically on both operands); V^T fragments are
+//    read from the key-major K tile with the LDS transpose read.  O (512 x 32 per wave) stays in
+//    256 accumulation registers.
+//  * K tiles of 32 keys are staged by direct global->LDS 16-byte loads into a double buffer:
+//    kqk[32][512] holds rotated dims 0..127 and raw dims 128..511 (QK operand), vlo[32][128]
+//    holds raw dims 0..127 (the rest of the V operand).  16-byte chunks are XOR-swizzled per row
+//    so that both the 8-row b128 reads and the 4-row transpose reads hit distinct banks.
+//  * Online softmax in the log2 domain with a lazy rescale: the running maximum is only moved
+//    when a tile exceeds it by more than 8 (so exp2 arguments stay <= 8 and P fits bf16), which
+//    keeps the 256-register O rescale off the common path.
+//  * Workgroups are launched latest query block first (longest causal work first).
+#include "common.h"
+
+namespace dca {
+namespace {
+
+constexpr int kD = 512;
+constexpr int kRot = 128;
+constexpr int kNK = 32;                          // keys per tile
+constexpr int kKqkBytes = kNK * kD * 2;          // 32 KiB
+constexpr int kVloBytes = kNK * kRot * 2;        // 8 KiB
+constexpr int kStageBytes = kKqkBytes + kVloBytes;
+constexpr float kTau = 8.0f;                     // lazy-rescale threshold (log2 units)
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+__device__ __forceinline__ void dma16(const void* src, char* lds_row_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_row_base, 16, 0, 0);
+}
+
+template <int G>
+__global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_qblocks) {
+  constexpr int QB = 128 / G;  // query positions per workgroup
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kStageBytes];
+  __shared__ int s_lo[3][QB], s_hi[3][QB];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, n = l & 31, half = l >> 5;
+  const int per = a.B * a.Hkv;
+  const int qb = n_qblocks - 1 - (int)(blockIdx.x / per);
+  const int bg = (int)(blockIdx.x % per);
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int64_t rows = (int64_t)a.B * a.T;
+  const float scale_log2 = a.scale * kLog2e;
+
+  // ---- per-position intervals of the three regimes -------------------------------------
+  if (tid < 3 * QB) {
+    const int r = tid / QB, p = tid % QB;
+    const int t = qb * QB + p;
+    int lo = 0, hi = -1;
+    if (t < a.T) {
+      lo = max(a.bounds[(r * rows + (int64_t)b * a.T + t) * 2 + 0], 0);
+      hi = min(a.bounds[(r * rows + (int64_t)b * a.T + t) * 2 + 1], a.n_kv - 1);
+    }
+    s_lo[r][p] = lo;
+    s_hi[r][p] = hi;
+  }
+
+  // ---- this lane's query row ----------------------------------------------------------------
+  const int rho = 32 * w + n;
+  const int pos_in_blk = rho / G, hh = rho % G;
+  const int t = qb * QB + pos_in_blk;
+  const bool row_valid = t < a.T;
+  const int tt = row_valid ? t : a.T - 1;
+  const int64_t rowhead = ((int64_t)b * a.T + tt) * a.Hq + (int64_t)g * G + hh;
+
+  bf16x8 q[32];
+  {
+    const bf16* qt = (const bf16*)a.q_tail + rowhead * a.q_tail_hs + 8 * half;
+#pragma unroll
+    for (int s = 8; s < 32; ++s) q[s] = *(const bf16x8*)(qt + 16 * s - kRot);
+  }
+
+  // LDS read offsets (bytes).  QK operand: row n, chunk (2s + half) ^ swz(n).
+  int qk_off[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) qk_off[u] = n * 1024 + 16 * ((2 * u + half) ^ swz(n & 7));
+  // V^T operand (transpose read): row 4*half + (l%16)/4 (+ 16 ks + 8 e), dims
+  // 32 dt + 16 grp + 4 (j%4); chunk 4 dt + c0 with c0 = 2 grp + (j/2)%2, byte (j%2)*8.
+  const int j16 = l & 15, grp = (l >> 4) & 1;
+  const int rho_l = 4 * half + (j16 >> 2);
+  const int sw = swz(rho_l & 7);
+  const int c0 = 2 * grp + ((j16 >> 1) & 1);
+  const int b2 = sw >> 2;
+  const int cpart = 16 * (c0 ^ (sw & 3)) + 8 * (j16 & 1);
+  const int v_lo_even = rho_l * 256 + cpart + 64 * b2, v_lo_odd = rho_l * 256 + cpart - 64 * b2;
+  const int v_hi_even = rho_l * 1024 + cpart + 64 * b2, v_hi_odd = rho_l * 1024 + cpart - 64 * b2;
+
+  __syncthreads();
+
+  const int64_t kv_stride = (int64_t)a.Hkv;
+  const bf16* kraw_b = (const bf16*)a.k_raw + ((int64_t)b * a.n_kv * kv_stride + g) * kD;
+  const bf16* krot_b = (const bf16*)a.k_rot + ((int64_t)b * a.n_kv * kv_stride + g) * a.k_rot_hs;
+
+  for (int r = 0; r < 3; ++r) {
+    if (!a.o[r]) continue;
+    // union of the rows' intervals and the range where no row needs masking
+    int umin = 0x7fffffff, umax = -1, fmax_lo = -0x7fffffff, fmin_hi = 0x7fffffff;
+    for (int p = 0; p < QB; ++p) {
+      const int lo = s_lo[r][p], hi = s_hi[r][p];
+      if (lo <= hi) {
+        umin = min(umin, lo);
+        umax = max(umax, hi);
+      }
+      fmax_lo = max(fmax_lo, lo);
+      fmin_hi = min(fmin_hi, hi);
+    }
+    const int my_lo = s_lo[r][pos_in_blk], my_hi = s_hi[r][pos_in_blk];
+
+    {
+      const bf16* qr = (const bf16*)a.q_rot[r] + rowhead * a.q_rot_hs + 8 * half;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) q[s] = *(const bf16x8*)(qr + 16 * s);
+    }
+    f32x16 o[16];
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) o[dt] = f32x16{};
+    float m_used = -INFINITY, l_part = 0.0f;
+
+    if (umin <= umax) {
+      const int kt0 = umin / kNK, kt1 = umax / kNK;
+      auto issue = [&](int buf, int k0) {
+        char* kqk = smem + buf * kStageBytes;
+        char* vlo = kqk + kKqkBytes;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int row = 8 * w + i;
+          int key = k0 + row;
+          key = key < a.n_kv ? key : a.n_kv - 1;
+          const int c = l ^ swz(row & 7);
+          const bf16* src = c < 16 ? krot_b + (int64_t)key * kv_stride * a.k_rot_hs + 8 * c
+                                   : kraw_b + (int64_t)key * kv_stride * kD + 8 * c;
+          dma16(src, kqk + row * 1024);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int row = 8 * w + 4 * i + (l >> 4);
+          int key = k0 + row;
+          key = key < a.n_kv ? key : a.n_kv - 1;
+          const int c = (l & 15) ^ swz(row & 7);
+          dma16(kraw_b + (int64_t)key * kv_stride * kD + 8 * c, vlo + (8 * w + 4 * i) * 256);
+        }
+      };
+
+      issue(0, kt0 * kNK);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+
+      for (int kt = kt0; kt <= kt1; ++kt) {
+        const int cur = (kt - kt0) & 1;
+        const int k0 = kt * kNK;
+        if (kt < kt1) issue(cur ^ 1, k0 + kNK);
+        const char* kqk = smem + cur * kStageBytes;
+        const char* vlo = kqk + kKqkBytes;
+
+        // S^T = K Q^T over all 512 dims
+        f32x16 sacc = f32x16{};
+#pragma unroll
+        for (int s = 0; s < 32; ++s) {
+          const bf16x8 kf = *(const bf16x8*)(kqk + qk_off[s & 3] + 128 * (s >> 2));
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, q[s], sacc, 0, 0, 0);
+        }
+        const bool full = fmax_lo <= k0 && k0 + kNK - 1 <= fmin_hi;
+        float sv[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          sv[e] = sacc[e] * scale_log2;
+          if (!full) {
+            const int key = k0 + 8 * (e >> 2) + 4 * half + (e & 3);
+            if (key < my_lo || key > my_hi) sv[e] = -INFINITY;
+          }
+        }
+        float mx = sv[0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sv[e]);
+        {
+          auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                      false, false);
+          mx = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1]));
+        }
+        const bool need = mx > m_used + kTau;
+        if (__ballot(need)) {
+          const float m_new = need ? mx : m_used;
+          const float alpha = exp2f(m_used - m_new);
+          l_part *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 16; ++dt) o[dt] *= alpha;
+          m_used = m_new;
+        }
+        float p[16];
+        float psum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          p[e] = sv[e] == -INFINITY ? 0.0f : exp2f(sv[e] - m_used);
+          psum += p[e];
+        }
+        l_part += psum;
+        bf16x8 pk0, pk1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pk0[e] = (bf16)p[e];
+          pk1[e] = (bf16)p[8 + e];
+        }
+        // O^T += V^T P^T
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8 pb = ks ? pk1 : pk0;
+#pragma unroll
+          for (int dt = 0; dt < 16; ++dt) {
+            const bool lo_part = dt < 4;
+            const char* base = lo_part ? vlo : kqk;
+            const int stride = lo_part ? 256 : 1024;
+            const int off = ((dt & 1) ? (lo_part ? v_lo_odd : v_hi_odd)
+                                      : (lo_part ? v_lo_even : v_hi_even)) + 64 * dt;
+            const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (lds_bf16x4*)(base + off + (16 * ks) * stride));
+            const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (lds_bf16x4*)(base + off + (16 * ks + 8) * stride));
+            bf16x8 vf;
+            vf[0] = v0[0]; vf[1] = v0[1]; vf[2] = v0[2]; vf[3] = v0[3];
+            vf[4] = v1[0]; vf[5] = v1[1]; vf[6] = v1[2]; vf[7] = v1[3];
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o[dt], 0, 0, 0);
+          }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+      }
+    }
+
+    // ---- epilogue: normalise and store this regime's partial --------------------------------
+    float l_tot;
+    {
+      auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part),
+                                                  false, false);
+      l_tot = __uint_as_float(sw2[0]) + __uint_as_float(sw2[1]);
+    }
+    const bool nonempty = l_tot > 0.0f;
+    const float inv = nonempty ? 1.0f / l_tot : 0.0f;
+    if (row_valid) {
+      float* orow = a.o[r] + rowhead * kD + 4 * half;
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          f32x4 v;
+          v[0] = o[dt][4 * q4 + 0] * inv;
+          v[1] = o[dt][4 * q4 + 1] * inv;
+          v[2] = o[dt][4 * q4 + 2] * inv;
+          v[3] = o[dt][4 * q4 + 3] * inv;
+          *(f32x4*)(orow + 32 * dt + 8 * q4) = v;
+        }
+      }
+      if (half == 0)
+        a.lse[r][rowhead] = nonempty ? (m_used + log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_prefill_bf16(const AttnArgs& a, hipStream_t stream) {
+  const int G = a.Hq / a.Hkv;
+  const int QB = 128 / G;
+  const int n_qblocks = (a.T + QB - 1) / QB;
+  const int64_t blocks = (int64_t)n_qblocks * a.B * a.Hkv;
+  if (blocks <= 0) return hipSuccess;
+  dim3 grid((unsigned)blocks), block(256);
+  switch (G) {
+    case 1: hipLaunchKernelGGL(attn_prefill_kernel<1>, grid, block, 0, stream, a, n_qblocks); break;
+    case 2: hipLaunchKernelGGL(attn_prefill_kernel<2>, grid, block, 0, stream, a, n_qblocks); break;
+    case 4: hipLaunchKernelGGL(attn_prefill_kernel<4>, grid, block, 0, stream, a, n_qblocks); break;
+    case 8: hipLaunchKernelGGL(attn_prefill_kernel<8>, grid, block, 0, stream, a, n_qblocks); break;
+    case 16: hipLaunchKernelGGL(attn_prefill_kernel<16>, grid, block, 0, stream, a, n_qblocks); break;
+    case 32: hipLaunchKernelGGL(attn_prefill_kernel<32>, grid, block, 0, stream, a, n_qblocks); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dca

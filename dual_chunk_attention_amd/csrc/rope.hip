@@ -1,0 +1,106 @@
+// Partial ("proportional") RoPE at explicit positions.
+// DCA feature page: "DCA algorithm" (only the rotary dims are remapped, the rest pass through),
+// "Why llamafile is sufficient" (per-pair freq_factors fed to the rope), "Section C2b" (keys
+// rotated once, queries three times).  Pair f couples dims f and f + n_rot/2; its angle is
+// p * theta^(-2f/n_rot) / freq_factors[f], formed and reduced in fp64; the rotation itself is
+// fp32 and rounds to nearest-even on a bf16 store.
+#include "common.h"
+
+namespace dca {
+namespace {
+
+constexpr int kRopeRows = 4;   // rows per block
+
+template <typename T>
+__global__ __launch_bounds__(256) void rope_kernel(RopeArgs a) {
+  __shared__ double w_s[512];
+  const int half = a.n_rot / 2;
+  for (int f = threadIdx.x; f < half; f += blockDim.x) {
+    double w = pow(a.theta, -2.0 * (double)f / (double)a.n_rot);
+    if (a.freq_factors) w /= (double)a.freq_factors[f];
+    w_s[f] = w;
+  }
+  __syncthreads();
+  const int z = blockIdx.z;
+  const T* __restrict__ x = (const T*)a.x;
+  T* __restrict__ y = (T*)a.y + (int64_t)z * a.y_plane_stride;
+  const int64_t row0 = (int64_t)blockIdx.x * kRopeRows;
+  const int n = kRopeRows * half;
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    const int64_t row = row0 + e / half;
+    const int f = e % half;
+    if (row >= a.rows) continue;
+    int64_t p;
+    if (a.pos) {
+      p = a.pos[(int64_t)z * a.pos_plane_stride + row];
+    } else {
+      p = (row % a.pos_mod_rows) % a.chunk;
+    }
+    double sd, cd;
+    sincos((double)p * w_s[f], &sd, &cd);
+    const float cs = (float)cd, sn = (float)sd;
+    for (int h = 0; h < a.n_heads; ++h) {
+      const T* xr = x + row * a.x_row_stride + (int64_t)h * a.x_head_stride;
+      T* yr = y + row * a.y_row_stride + (int64_t)h * a.y_head_stride;
+      const float x0 = to_f32(xr[f]);
+      const float x1 = to_f32(xr[f + half]);
+      yr[f] = from_f32<T>(fmaf(x0, cs, -x1 * sn));
+      yr[f + half] = from_f32<T>(fmaf(x0, sn, x1 * cs));
+    }
+  }
+  if (a.copy_tail) {
+    const int tail = a.head_dim - a.n_rot;
+    const int m = kRopeRows * a.n_heads * tail;
+    for (int e = threadIdx.x; e < m; e += blockDim.x) {
+      const int64_t row = row0 + e / (a.n_heads * tail);
+      const int rem = e % (a.n_heads * tail);
+      const int h = rem / tail, d = a.n_rot + rem % tail;
+      if (row >= a.rows) continue;
+      y[row * a.y_row_stride + (int64_t)h * a.y_head_stride + d] =
+          x[row * a.x_row_stride + (int64_t)h * a.x_head_stride + d];
+    }
+  }
+}
+
+__global__ void rope_tables_kernel(float2* lo, float2* hi, int32_t n_hi, int32_t n_rot,
+                                   double theta, const float* ff) {
+  const int half = n_rot / 2;
+  const int64_t total = (int64_t)(64 + n_hi) * half;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = e / half;
+    const int f = (int)(e % half);
+    double w = pow(theta, -2.0 * (double)f / (double)n_rot);
+    if (ff) w /= (double)ff[f];
+    const double p = r < 64 ? (double)r : 64.0 * (double)(r - 64);
+    double sd, cd;
+    sincos(p * w, &sd, &cd);
+    float2 v = make_float2((float)cd, (float)sd);
+    if (r < 64) lo[r * half + f] = v;
+    else hi[(r - 64) * half + f] = v;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rope(const RopeArgs& a, bool bf16_data, hipStream_t stream) {
+  if (a.rows <= 0 || a.planes <= 0) return hipSuccess;
+  dim3 grid((unsigned)((a.rows + kRopeRows - 1) / kRopeRows), 1, (unsigned)a.planes);
+  if (bf16_data)
+    hipLaunchKernelGGL(rope_kernel<bf16>, grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(rope_kernel<float>, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_tables(float2* lo, float2* hi, int32_t n_hi, int32_t n_rot, double theta,
+                              const float* freq_factors, hipStream_t stream) {
+  int64_t total = (int64_t)(64 + n_hi) * (n_rot / 2);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  hipLaunchKernelGGL(rope_tables_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, lo, hi,
+                     n_hi, n_rot, theta, freq_factors);
+  return hipGetLastError();
+}
+
+}  // namespace dca

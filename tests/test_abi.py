@@ -1,0 +1,89 @@
+"""C-ABI library checks that need no GPU: it loads, exports every entry point that include/dca.h
+declares, and rejects bad arguments with a status code before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from dual_chunk_attention_amd import dca
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "dca.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dca_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_five_operations():
+    names = declared_functions()
+    for f in ["dca_remap_positions", "dca_rope_partial", "dca_attn_regime", "dca_lse_merge",
+              "dca_attention", "dca_attention_workspace_size", "dca_attn_regime_workspace_size",
+              "dca_last_error"]:
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol():
+    if not os.path.exists(dca.LIB_PATH):
+        pytest.skip("libdca.so not built")
+    L = dca.lib()
+    for f in declared_functions():
+        assert hasattr(L, f), f"{f} not exported"
+
+
+def _cfg(**kw):
+    base = dict(head_dim=512, n_rot=128, n_head_q=16, n_head_kv=2, chunk=1024)
+    base.update(kw)
+    return dca.Config(**base).c()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=0), dca.ERR_INVALID_ARGUMENT),
+    (dict(n_rot=3), dca.ERR_INVALID_ARGUMENT),
+    (dict(n_rot=1024), dca.ERR_INVALID_ARGUMENT),
+    (dict(n_head_q=15), dca.ERR_INVALID_ARGUMENT),
+    (dict(chunk=0), dca.ERR_INVALID_ARGUMENT),
+    (dict(remap_mode=1), dca.ERR_UNSUPPORTED),
+    (dict(head_dim=256), dca.ERR_UNSUPPORTED),   # bf16 path is head_dim 512 only
+    (dict(n_head_q=64, n_head_kv=1), dca.ERR_UNSUPPORTED),
+])
+def test_attention_rejects_bad_config(kw, code):
+    if not os.path.exists(dca.LIB_PATH):
+        pytest.skip("libdca.so not built")
+    L = dca.lib()
+    c = _cfg(**kw)
+    st = L.dca_attention(ctypes.byref(c), dca.BF16, 1, 4, ctypes.c_void_p(16), ctypes.c_void_p(16),
+                         ctypes.c_void_p(16), 4, dca.BF16, ctypes.c_void_p(16), None,
+                         ctypes.c_void_p(16), 1 << 30, None)
+    assert st == code
+    assert L.dca_last_error().decode() != ""
+    assert L.dca_attention_workspace_size(ctypes.byref(c), dca.BF16, 1, 4, 4) == 0
+
+
+def test_other_validation_paths():
+    if not os.path.exists(dca.LIB_PATH):
+        pytest.skip("libdca.so not built")
+    L = dca.lib()
+    c = _cfg()
+    vp = ctypes.c_void_p(16)
+    assert L.dca_attention(ctypes.byref(c), dca.BF16, -1, 4, vp, vp, vp, 4, dca.BF16, vp, None, vp,
+                           1 << 30, None) == dca.ERR_INVALID_ARGUMENT
+    assert L.dca_attention(ctypes.byref(c), dca.BF16, 1, 4, None, vp, vp, 4, dca.BF16, vp, None, vp,
+                           1 << 30, None) == dca.ERR_INVALID_ARGUMENT
+    need = L.dca_attention_workspace_size(ctypes.byref(c), dca.BF16, 1, 4096, 4096)
+    assert need > 0
+    assert L.dca_attention(ctypes.byref(c), dca.BF16, 1, 4096, vp, vp, vp, 4096, dca.BF16, vp, None,
+                           vp, need - 1, None) == dca.ERR_WORKSPACE_TOO_SMALL
+    assert L.dca_attn_regime(ctypes.byref(c), dca.BF16, 3, 1, 4, vp, vp, vp, vp, 4, vp, vp, None, 0,
+                             None) == dca.ERR_INVALID_ARGUMENT
+    parts = (ctypes.c_void_p * 9)(*([16] * 9))
+    assert L.dca_lse_merge(9, parts, parts, 4, 512, dca.F32, vp, vp, None) == dca.ERR_INVALID_ARGUMENT
+    assert L.dca_lse_merge(0, parts, parts, 4, 512, dca.F32, vp, vp, None) == dca.ERR_INVALID_ARGUMENT
+    c0 = _cfg(chunk=0)
+    assert L.dca_remap_positions(ctypes.byref(c0), 1, 4, vp, 4, vp, vp, vp, None) == dca.ERR_INVALID_ARGUMENT
+    assert L.dca_rope_partial(ctypes.byref(c), 7, vp, 4, 2, vp, vp, None) == dca.ERR_INVALID_ARGUMENT
+    # empty work is a no-op that succeeds
+    assert L.dca_attention(ctypes.byref(c), dca.BF16, 0, 4, None, None, None, 4, dca.BF16, None,
+                           None, None, 0, None) == dca.OK

@@ -1,0 +1,311 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle on the same seeded inputs.
+
+Integer outputs (positions, intervals) must match bit-exactly; O within 1e-2 absolute and LSE within
+1e-3 relative (see gpu_util).  Large workloads are checked on stratified sampled rows (every chunk's
+local offsets 0, 1, c/2, c-2, c-1, plus random rows); small ones on every row.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dual_chunk_attention_amd import dca, synth
+from gpu_util import (assert_lse_close, assert_o_close, cfg_for, dev, rows_of, sample_rows, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(w, **kw):
+    inp = synth.make_inputs(w, **kw)
+    w = inp["w"]
+    ff = to_dev(inp["freq_factors"]) if w.ff_uniform else None
+    return inp, w, ff
+
+
+def _oracle_attention(inp, w, rows=None, chunk=None, per_regime=True):
+    ff = inp["freq_factors"].astype(np.float64) if w.ff_uniform else None
+    return oracle.attention(inp["q"], inp["q_pos"], inp["k"], chunk=w.chunk if chunk is None else chunk,
+                            n_rot=w.n_rot, theta=w.theta, scale=w.scale, freq_factors=ff, rows=rows,
+                            per_regime=per_regime)
+
+
+# ----------------------------------------------------------------------------------------------
+# a1: remap, bit-exact
+# ----------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_remap_bit_exact_on_workloads(name):
+    w = synth.WORKLOADS[name]
+    q_pos = (w.q0 + np.arange(w.T, dtype=np.int64)).astype(np.int32)
+    q_pos = np.ascontiguousarray(np.broadcast_to(q_pos, (w.B, w.T)))
+    pos_q, pos_k, bounds = dca.remap_positions(cfg_for(w), to_dev(q_pos), w.N)
+    torch.cuda.synchronize()
+    o_pq, o_pk, o_b, st = oracle.remap(w.chunk, q_pos, w.N)
+    assert st == 0
+    assert np.array_equal(pos_q.cpu().numpy().reshape(3, -1), o_pq)
+    assert np.array_equal(pos_k.cpu().numpy(), o_pk)
+    assert np.array_equal(bounds.cpu().numpy().reshape(3, -1, 2), o_b)
+
+
+@pytest.mark.parametrize("c,n_kv", [(1, 50), (7, 100), (64, 64), (1000, 300), (5, 0)])
+def test_remap_bit_exact_edge_positions(c, n_kv):
+    q_pos = np.array([[-5, -1, 0, 1, 6, 7, 8, 49, 63, 64, 99, 100, 299, 300, 1 << 30]], np.int32)
+    cfg = dca.Config(chunk=c)
+    pos_q, pos_k, bounds = dca.remap_positions(cfg, to_dev(q_pos), n_kv)
+    torch.cuda.synchronize()
+    o_pq, o_pk, o_b, st = oracle.remap(c, q_pos, n_kv)
+    assert np.array_equal(pos_q.cpu().numpy().reshape(3, -1), o_pq)
+    assert np.array_equal(pos_k.cpu().numpy(), o_pk)
+    assert np.array_equal(bounds.cpu().numpy().reshape(3, -1, 2), o_b)
+
+
+# ----------------------------------------------------------------------------------------------
+# a2: partial RoPE
+# ----------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bf16", [True, False])
+@pytest.mark.parametrize("inplace", [False, True])
+def test_rope_partial(bf16, inplace):
+    rng = np.random.default_rng(5)
+    rows, H, D, n_rot = 96, 16, 512, 128
+    x32 = rng.standard_normal((rows, H, D)).astype(np.float32)
+    pos = np.concatenate([[0, 1, 2, 8191, 8192, 65535, 131071, 1048575, (1 << 31) - 1],
+                          rng.integers(0, 1 << 21, rows - 9)]).astype(np.int32)
+    ff = rng.uniform(1, 8, n_rot // 2).astype(np.float32)
+    if bf16:
+        xb = synth.bf16_bits(x32)
+        x_ref = synth.bf16_to_f32(xb).astype(np.float64)
+        xd = to_dev(xb)
+    else:
+        x_ref = x32.astype(np.float64)
+        xd = to_dev(x32)
+    cfg = dca.Config(head_dim=D, n_rot=n_rot, n_head_q=H, n_head_kv=H, freq_factors=to_dev(ff))
+    x_in = xd.clone()
+    y = dca.rope_partial(cfg, x_in, to_dev(pos), out=x_in if inplace else None)
+    torch.cuda.synchronize()
+    got = y.float().cpu().numpy().astype(np.float64)
+    want = oracle.rope(x_ref, pos, n_rot, 1.0e6, ff.astype(np.float64))
+    # dims >= n_rot: bit-exact copy
+    assert np.array_equal(got[..., n_rot:], x_ref[..., n_rot:])
+    # rotated dims: fp32 rotation of fp64 angles, then (bf16) round to nearest
+    err = np.abs(got[..., :n_rot] - want[..., :n_rot])
+    mag = np.abs(x_ref[..., :n_rot // 2]) + np.abs(x_ref[..., n_rot // 2:n_rot])
+    mag = np.concatenate([mag, mag], axis=-1)
+    bound = (2.0 ** -8 * np.abs(want[..., :n_rot]) if bf16 else 0.0) + 2e-6 * mag + 1e-30
+    assert (err <= bound).all(), float((err / bound).max())
+
+
+# ----------------------------------------------------------------------------------------------
+# a5: N-way LSE merge
+# ----------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n_parts", [1, 2, 3, 8])
+@pytest.mark.parametrize("out_bf16", [False, True])
+def test_lse_merge(n_parts, out_bf16):
+    rng = np.random.default_rng(n_parts)
+    rows, D = 1000, 512
+    o = rng.standard_normal((n_parts, rows, D)).astype(np.float32)
+    l = (rng.standard_normal((n_parts, rows)) * 5).astype(np.float32)
+    l[:, :7] = -np.inf                                  # all parts empty
+    l[rng.random((n_parts, rows)) < 0.3] = -np.inf      # some parts empty
+    o[np.isneginf(l)] = np.nan                          # an empty part's O must never be read
+    got_o, got_l = dca.lse_merge([to_dev(o[p]) for p in range(n_parts)], [to_dev(l[p]) for p in range(n_parts)],
+                                 torch.bfloat16 if out_bf16 else torch.float32)
+    torch.cuda.synchronize()
+    want_o, want_l = oracle.merge(np.nan_to_num(o.astype(np.float64)), l.astype(np.float64))
+    g = got_o.float().cpu().numpy()
+    tol = 2.0 ** -8 * np.abs(want_o) + 1e-5 if out_bf16 else 1e-5
+    assert np.isfinite(g).all()
+    assert (np.abs(g - want_o) <= tol).all()
+    assert_lse_close(got_l.cpu().numpy(), want_l, rtol=1e-6)
+    assert (g[:7] == 0).all() and np.isneginf(got_l.cpu().numpy()[:7]).all()
+
+
+# ----------------------------------------------------------------------------------------------
+# a3/a4: one regime pass at a time, against the oracle's per-regime partials
+# ----------------------------------------------------------------------------------------------
+
+REGIME_CASES = [
+    # (label, workload name, overrides, chunk override, rows sampled (None = all))
+    ("fp32-tiny", "prefill-256-c64-fp32", {}, None, None),
+    ("bf16-prefill-ragged", "prefill-4k-c1024", dict(T=300, N=300), 64, None),
+    ("bf16-prefill-offset", "prefill-4k-c1024", dict(T=200, q0=700, N=1000), 128, None),
+    ("bf16-decode", "decode-b8-kv256k-c65536", dict(B=2, N=20000, q0=19999), 4096, None),
+    ("bf16-decode-midchunk", "decode-b8-kv256k-c65536", dict(B=2, T=3, N=9000, q0=8000), 3000, None),
+]
+
+
+@pytest.mark.parametrize("label,name,over,chunk,rows", REGIME_CASES, ids=[c[0] for c in REGIME_CASES])
+def test_attn_regime_each_regime(label, name, over, chunk, rows):
+    inp, w, ffd = _inputs(name, **over)
+    B, T = inp["q"].shape[:2]
+    N = inp["k"].shape[1]
+    cfg = cfg_for(w, ffd, chunk=chunk)
+    c = cfg.chunk
+    q, k, qp = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["q_pos"])
+    pos_q, pos_k, bounds = dca.remap_positions(cfg, qp, N)
+    k_rot = dca.rope_partial(cfg, k.reshape(B * N, w.Hkv, w.D), pos_k.repeat(B)).reshape(k.shape)
+    res = _oracle_attention(inp, w, chunk=c)
+    for r in range(3):
+        q_r = dca.rope_partial(cfg, q.reshape(B * T, w.Hq, w.D), pos_q[r].reshape(-1).contiguous())
+        o_r, l_r = dca.attn_regime(cfg, r, q_r.reshape(q.shape), bounds, k_rot, k)
+        torch.cuda.synchronize()
+        want_o = res["o_reg"][r].reshape(B, T, w.Hq, w.D)
+        want_l = res["lse_reg"][r].reshape(B, T, w.Hq)
+        assert_o_close(o_r.cpu().numpy(), want_o, atol=1e-4 if w.dtype == "f32" else 1e-2, what=f"O_{r}")
+        assert_lse_close(l_r.cpu().numpy(), want_l, rtol=1e-5 if w.dtype == "f32" else 1e-3, what=f"lse_{r}")
+        # an empty regime is exactly (0, -inf)
+        empty = np.isneginf(want_l)
+        assert (o_r.cpu().numpy()[empty] == 0).all()
+
+
+# ----------------------------------------------------------------------------------------------
+# the whole path: dca_attention on every workload
+# ----------------------------------------------------------------------------------------------
+
+E2E = [
+    ("prefill-256-c64-fp32", None, torch.float32),
+    ("prefill-4k-c1024", 96, torch.bfloat16),
+    ("prefill-32k-c8192", 48, torch.bfloat16),
+    ("decode-b8-kv256k-c65536", 0, torch.bfloat16),
+    ("prefill-4k-at-1m-c65536", 4, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("name,n_random,o_dtype", E2E, ids=[e[0] for e in E2E])
+def test_attention_end_to_end(name, n_random, o_dtype):
+    inp, w, ffd = _inputs(name)
+    B, T = w.B, w.T
+    if n_random is None:
+        rows = None
+    elif w.T == 1:
+        rows = rows_of(B, T, [(b, 0) for b in range(B)])
+    elif w.q0 > 0:   # slice: few rows (each costs ~1M keys in the oracle)
+        rows = rows_of(B, T, [(0, 0), (0, 1), (0, 2047), (0, 4094), (0, 4095)] +
+                       [(0, int(t)) for t in np.random.default_rng(9).integers(0, T, n_random)])
+    else:
+        rows = rows_of(B, T, sample_rows(T, w.chunk, n_random, seed=w.seed))
+    q, k, qp = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["q_pos"])
+    o, lse = dca.attention(cfg_for(w, ffd), q, qp, k, o_dtype=o_dtype)
+    torch.cuda.synchronize()
+    res = _oracle_attention(inp, w, rows=rows, per_regime=False)
+    sel = res["rows"]
+    got_o = o.float().cpu().numpy().reshape(B * T, w.Hq, w.D)[sel]
+    got_l = lse.cpu().numpy().reshape(B * T, w.Hq)[sel]
+    assert_o_close(got_o, res["o"], atol=1e-4 if w.dtype == "f32" else 1e-2)
+    assert_lse_close(got_l, res["lse"], rtol=1e-5 if w.dtype == "f32" else 1e-3)
+
+
+# ----------------------------------------------------------------------------------------------
+# structured probes (random inputs make |O| ~ N^-1/2, too small for a 1e-2 bound to bite)
+# ----------------------------------------------------------------------------------------------
+
+def _probe_inputs(T, N, q0, seed, kind):
+    w = synth.Workload("probe", 1, T, q0, N, 256, 16, 2, "bf16", seed)
+    inp = synth.make_inputs(w)
+    q = synth.bf16_to_f32(inp["q"]).copy()
+    k = synth.bf16_to_f32(inp["k"]).copy()
+    rng = np.random.default_rng(seed + 1)
+    if kind == "distance":
+        # q: rotary part a unit vector in pair 0 scaled by 6, tail zero; k: rotary part the
+        # orthogonal unit vector of pair 0 (so s = scale*6*sin(d w_0)), tail random.
+        q[..., :] = 0.0
+        q[..., 0] = 6.0 * np.sqrt(512)
+        k[..., :128] = 0.0
+        k[..., 64] = 1.0
+    else:  # needles: a few keys equal to a scaled copy of a query's tail
+        for t in rng.integers(0, T, 24):
+            i = q0 + t
+            for j in {int(i), int(max(0, i - 3)), int(max(0, i - 300)), int(rng.integers(0, i + 1))}:
+                for g in range(2):
+                    k[0, j, g, 128:] = 3.0 * q[0, t, 8 * g + int(rng.integers(0, 8)), 128:] / np.sqrt(np.mean(q[0, t, 0, 128:] ** 2))
+    inp["q"], inp["k"] = synth.bf16_bits(q), synth.bf16_bits(k)
+    return inp, w
+
+
+@pytest.mark.parametrize("kind", ["distance", "needles"])
+@pytest.mark.parametrize("T,N,q0", [(1024, 1024, 0), (1, 3000, 2999), (256, 2000, 1744)])
+def test_structured_probes(kind, T, N, q0):
+    inp, w = _probe_inputs(T, N, q0, seed=31 + T, kind=kind)
+    ffd = to_dev(inp["freq_factors"])
+    cfg = cfg_for(w, ffd)
+    o, lse = dca.attention(cfg, to_dev(inp["q"]), to_dev(inp["q_pos"]), to_dev(inp["k"]), o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = None if T <= 256 else rows_of(1, T, sample_rows(T, w.chunk, 64, seed=3))
+    res = _oracle_attention(inp, w, rows=rows, per_regime=False)
+    sel = res["rows"]
+    got_o = o.cpu().numpy().reshape(T, w.Hq, w.D)[sel]
+    assert np.abs(res["o"]).max() > 0.3          # the probe really produces large outputs
+    assert_o_close(got_o, res["o"])
+    assert_lse_close(lse.cpu().numpy().reshape(T, w.Hq)[sel], res["lse"])
+
+
+# ----------------------------------------------------------------------------------------------
+# invariants across paths
+# ----------------------------------------------------------------------------------------------
+
+def test_chunk_covering_sequence_is_plain_attention():
+    """c >= seqlen: every row is intra-only; succ/inter partials are exactly empty."""
+    inp, w, ffd = _inputs("prefill-4k-c1024", T=512, N=512)
+    cfg = cfg_for(w, ffd, chunk=4096)
+    o, lse = dca.attention(cfg, to_dev(inp["q"]), to_dev(inp["q_pos"]), to_dev(inp["k"]), o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    res = _oracle_attention(inp, w, chunk=4096, per_regime=True)
+    assert np.isneginf(res["lse_reg"][1:]).all()
+    assert_o_close(o.cpu().numpy().reshape(-1, w.Hq, w.D), res["o"])
+    assert_lse_close(lse.cpu().numpy().reshape(-1, w.Hq), res["lse"])
+
+
+def test_decode_row_matches_prefill_row():
+    """The split-KV decode path at position p equals row p of the prefill path (both on GPU)."""
+    inp, w, ffd = _inputs("prefill-4k-c1024", T=2048, N=2048)
+    cfg = cfg_for(w, ffd, chunk=512)
+    q, k = to_dev(inp["q"]), to_dev(inp["k"])
+    o_pf, l_pf = dca.attention(cfg, q, to_dev(inp["q_pos"]), k, o_dtype=torch.float32)
+    for p in [5, 511, 512, 1000, 2047]:
+        qd = q[:, p:p + 1].contiguous()
+        o_d, l_d = dca.attention(cfg, qd, to_dev(np.array([[p]], np.int32)), k, o_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert_o_close(o_d.cpu().numpy()[0, 0], o_pf.cpu().numpy()[0, p], atol=5e-3)
+        assert_lse_close(l_d.cpu().numpy()[0, 0], l_pf.cpu().numpy()[0, p], rtol=5e-4)
+
+
+@pytest.mark.parametrize("shape", ["prefill", "decode"])
+def test_bitwise_deterministic(shape):
+    if shape == "prefill":
+        inp, w, ffd = _inputs("prefill-4k-c1024", T=1024, N=1024)
+        cfg = cfg_for(w, ffd, chunk=256)
+    else:
+        inp, w, ffd = _inputs("decode-b8-kv256k-c65536", B=2, N=50000, q0=49999)
+        cfg = cfg_for(w, ffd, chunk=8192)
+    q, k, qp = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["q_pos"])
+    o1, l1 = dca.attention(cfg, q, qp, k)
+    o2, l2 = dca.attention(cfg, q, qp, k)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(2, 2), (4, 2), (8, 2), (16, 1)])
+def test_gqa_ratios_bf16(Hq, Hkv):
+    w = synth.Workload("gqa", 1, 160, 0, 160, 48, Hq, Hkv, "bf16", 77)
+    inp = synth.make_inputs(w)
+    ffd = to_dev(inp["freq_factors"])
+    o, lse = dca.attention(cfg_for(w, ffd), to_dev(inp["q"]), to_dev(inp["q_pos"]), to_dev(inp["k"]),
+                           o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    res = _oracle_attention(inp, w, per_regime=False)
+    assert_o_close(o.cpu().numpy().reshape(-1, Hq, 512), res["o"])
+    assert_lse_close(lse.cpu().numpy().reshape(-1, Hq), res["lse"])
+
+
+def test_batch_of_prefill_sequences():
+    w = synth.Workload("b3", 3, 130, 0, 130, 40, 16, 2, "bf16", 78)
+    inp = synth.make_inputs(w)
+    ffd = to_dev(inp["freq_factors"])
+    o, lse = dca.attention(cfg_for(w, ffd), to_dev(inp["q"]), to_dev(inp["q_pos"]), to_dev(inp["k"]),
+                           o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    res = _oracle_attention(inp, w, per_regime=False)
+    assert_o_close(o.cpu().numpy().reshape(-1, 16, 512), res["o"])
+    assert_lse_close(lse.cpu().numpy().reshape(-1, 16), res["lse"])
