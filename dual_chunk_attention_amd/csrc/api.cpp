@@ -13,6 +13,13 @@
 namespace {
 
 thread_local std::string g_err;
+thread_local hipEvent_t* g_stage_events = nullptr;
+
+// Records stage event i on `stream` when the caller installed stage events.
+hipError_t mark(int i, hipStream_t stream) {
+  if (!g_stage_events) return hipSuccess;
+  return hipEventRecord(g_stage_events[i], stream);
+}
 
 dca_status fail(dca_status st, const char* fmt, ...) {
   char buf[512];
@@ -100,7 +107,7 @@ AttnWorkspace attention_layout(const dca_config* cfg, dca_dtype dtype, int32_t B
   };
   w.pos_q = take(3 * rows * 4);
   w.bounds = take(3 * rows * 2 * 4);
-  w.qrot = take(3 * rows * Hq * R * es);
+  w.qrot = take(3 * rows * Hq * R * es);   // bf16 path: fp16, same size
   const bool dec = use_decode(dtype, T);
   w.krot = take(dec ? 0 : (size_t)B * n_kv * Hkv * R * es);
   if (dec) {
@@ -148,6 +155,7 @@ dca::RopeArgs rope_args_for_q(const dca_config* cfg, const void* q, int64_t rows
   ra.n_rot = cfg->n_rot;
   ra.head_dim = cfg->head_dim;
   ra.copy_tail = 0;
+  ra.out_f16 = 1;   // rotated operands of the bf16 path are fp16 (ignored for fp32 data)
   ra.planes = 3;
   ra.theta = (double)cfg->rope_theta;
   ra.freq_factors = cfg->freq_factors;
@@ -159,6 +167,13 @@ dca::RopeArgs rope_args_for_q(const dca_config* cfg, const void* q, int64_t rows
 extern "C" {
 
 const char* dca_last_error(void) { return g_err.c_str(); }
+
+dca_status dca_set_stage_events(hipEvent_t* events, int32_t n) {
+  if (events && n > 0 && n < DCA_N_STAGE_EVENTS)
+    return fail(DCA_ERR_INVALID_ARGUMENT, "need %d stage events, got %d", DCA_N_STAGE_EVENTS, n);
+  g_stage_events = (events && n > 0) ? events : nullptr;
+  return DCA_OK;
+}
 
 dca_status dca_remap_positions(const dca_config* cfg, int32_t B, int32_t T, const int32_t* q_pos,
                                int32_t n_kv, int32_t* pos_q, int32_t* pos_k, int32_t* bounds,
@@ -323,11 +338,14 @@ dca_status dca_attention(const dca_config* cfg, dca_dtype dtype, int32_t B, int3
   const size_t es = elem_size(dtype);
   const int64_t Hq = cfg->n_head_q, R = cfg->n_rot, D = cfg->head_dim;
 
+  if ((st = hip_status(mark(0, stream), "stage event"))) return st;
   if ((st = hip_status(dca::launch_remap(q_pos, rows, cfg->chunk, n_kv, pos_q, nullptr, bounds, stream),
                        "remap launch")))
     return st;
+  if ((st = hip_status(mark(1, stream), "stage event"))) return st;
   dca::RopeArgs rq = rope_args_for_q(cfg, q, rows, qrot, pos_q);
   if ((st = hip_status(dca::launch_rope(rq, dtype == DCA_BF16, stream), "rope(q) launch"))) return st;
+  if ((st = hip_status(mark(2, stream), "stage event"))) return st;
 
   dca::AttnArgs a{};
   for (int r = 0; r < 3; ++r) a.q_rot[r] = (const char*)qrot + (size_t)r * rows * Hq * R * es;
@@ -338,6 +356,7 @@ dca_status dca_attention(const dca_config* cfg, dca_dtype dtype, int32_t B, int3
   a.bounds = bounds;
   a.B = B; a.T = T; a.Hq = cfg->n_head_q; a.Hkv = cfg->n_head_kv; a.n_kv = n_kv;
   a.D = cfg->head_dim; a.n_rot = cfg->n_rot; a.scale = cfg->scale;
+  a.rot_f16 = dtype == DCA_BF16;
 
   if (dec) {
     float2* lo = (float2*)(ws + L.tab_lo);
@@ -345,6 +364,7 @@ dca_status dca_attention(const dca_config* cfg, dca_dtype dtype, int32_t B, int3
     if ((st = hip_status(dca::launch_rope_tables(lo, hi, L.n_hi, cfg->n_rot, (double)cfg->rope_theta,
                                                  cfg->freq_factors, stream), "rope tables launch")))
       return st;
+    if ((st = hip_status(mark(3, stream), "stage event"))) return st;
     dca::DecodeArgs da{};
     da.base = a;
     da.o_part = (float*)(ws + L.dec_o);
@@ -358,6 +378,7 @@ dca_status dca_attention(const dca_config* cfg, dca_dtype dtype, int32_t B, int3
     da.chunk = cfg->chunk;
     if ((st = hip_status(dca::launch_attn_decode_bf16(da, stream), "decode attention launch")))
       return st;
+    if ((st = hip_status(mark(4, stream), "stage event"))) return st;
     dca::MergeArgs m{};
     m.o_base = da.o_part;
     m.lse_base = da.lse_part;
@@ -369,7 +390,9 @@ dca_status dca_attention(const dca_config* cfg, dca_dtype dtype, int32_t B, int3
     m.D = cfg->head_dim;
     m.o_out = o;
     m.lse_out = lse;
-    return hip_status(dca::launch_merge_many(m, o_dtype == DCA_BF16, stream), "split merge launch");
+    if ((st = hip_status(dca::launch_merge_many(m, o_dtype == DCA_BF16, stream), "split merge launch")))
+      return st;
+    return hip_status(mark(5, stream), "stage event");
   }
 
   // keys rotated once at j mod c (rotary dims only)
@@ -390,10 +413,12 @@ dca_status dca_attention(const dca_config* cfg, dca_dtype dtype, int32_t B, int3
     rk.n_rot = cfg->n_rot;
     rk.head_dim = cfg->head_dim;
     rk.planes = 1;
+    rk.out_f16 = 1;
     rk.theta = (double)cfg->rope_theta;
     rk.freq_factors = cfg->freq_factors;
     if ((st = hip_status(dca::launch_rope(rk, dtype == DCA_BF16, stream), "rope(k) launch"))) return st;
   }
+  if ((st = hip_status(mark(3, stream), "stage event"))) return st;
   a.k_rot = krot;
   a.k_rot_hs = R;
   float* op = (float*)(ws + L.o_parts);
@@ -407,6 +432,7 @@ dca_status dca_attention(const dca_config* cfg, dca_dtype dtype, int32_t B, int3
   else
     st = hip_status(dca::launch_attn_prefill_bf16(a, stream), "prefill attention launch");
   if (st) return st;
+  if ((st = hip_status(mark(4, stream), "stage event"))) return st;
   dca::MergeArgs m{};
   for (int r = 0; r < 3; ++r) {
     m.o_ptr[r] = a.o[r];
@@ -417,7 +443,8 @@ dca_status dca_attention(const dca_config* cfg, dca_dtype dtype, int32_t B, int3
   m.D = cfg->head_dim;
   m.o_out = o;
   m.lse_out = lse;
-  return hip_status(dca::launch_merge(m, o_dtype == DCA_BF16, stream), "merge launch");
+  if ((st = hip_status(dca::launch_merge(m, o_dtype == DCA_BF16, stream), "merge launch"))) return st;
+  return hip_status(mark(5, stream), "stage event");
 }
 
 }  // extern "C"

@@ -32,12 +32,23 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 
-template <bool ROTATE>
+template <bool ROT16>
+__device__ __forceinline__ f32x4 mfma16_rot(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  if constexpr (ROT16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+}
+
+// ROTATE: rotate the keys in registers (K read once); ROT16: rotary operands are fp16.
+template <bool ROTATE, bool ROT16>
 __global__ __launch_bounds__(256, 1) void attn_decode_kernel(DecodeArgs da) {
   const AttnArgs& a = da.base;
   __shared__ __attribute__((aligned(1024))) char kbuf[2 * kTileBytes];
   __shared__ __attribute__((aligned(16))) bf16 pbuf[16 * kTile];     // P[head][key]
-  __shared__ float smax[4][16], ssum[4][16];
+  __shared__ float smax[4][16], ssum[4][16], wsum[4][16];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int hcol = l & 15, gq = l >> 4;   // column (query head) and 16-lane group
@@ -99,7 +110,9 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(DecodeArgs da) {
     f32x4 o[8];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{};
-    float m_used = -INFINITY, l_part = 0.0f;
+    // l_part: exact row sum (LSE); w_part: sum of the bf16 weights the PV product uses (O's
+    // normaliser, so that weights and normaliser agree)
+    float m_used = -INFINITY, l_part = 0.0f, w_part = 0.0f;
 
     const int kt0 = lo / kTile, kt1 = hi / kTile;
     auto issue = [&](int buf, int k0) {
@@ -108,7 +121,7 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(DecodeArgs da) {
       for (int i = 0; i < 16; ++i) {
         const int row = 16 * w + i;
         int key = k0 + row;
-        key = key < a.n_kv ? key : a.n_kv - 1;
+        key = min(max(key, 0), a.n_kv - 1);
         const int c = l ^ swz(row & 7);
         __builtin_amdgcn_global_load_lds(kraw_b + (int64_t)key * a.Hkv * kD + 8 * c,
                                          (lds_void*)(base + row * 1024), 16, 0, 0);
@@ -142,19 +155,29 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(DecodeArgs da) {
             const float cs = A.x * Bv.x - A.y * Bv.y;
             const float sn = A.y * Bv.x + A.x * Bv.y;
             const float x0 = (float)kf[s][e], x1 = (float)kf[s + 2][e];
-            kf[s][e] = (bf16)fmaf(x0, cs, -x1 * sn);
-            kf[s + 2][e] = (bf16)fmaf(x0, sn, x1 * cs);
+            const float y0 = fmaf(x0, cs, -x1 * sn), y1 = fmaf(x0, sn, x1 * cs);
+            if constexpr (ROT16) {
+              kf[s][e] = __builtin_bit_cast(bf16, (f16)y0);
+              kf[s + 2][e] = __builtin_bit_cast(bf16, (f16)y1);
+            } else {
+              kf[s][e] = (bf16)y0;
+              kf[s + 2][e] = (bf16)y1;
+            }
           }
         }
       } else {
-        const bf16* kr = krot_b + (int64_t)min(key, a.n_kv - 1) * a.Hkv * a.k_rot_hs + 8 * gq;
+        const bf16* kr = krot_b + (int64_t)min(key, a.n_kv - 1) * a.Hkv * a.k_rot_hs + 8 * gq;  // 2-byte elements
 #pragma unroll
         for (int s = 0; s < 4; ++s) kf[s] = *(const bf16x8*)(kr + 32 * s);
       }
       f32x4 sacc = f32x4{};
 #pragma unroll
-      for (int s = 0; s < 16; ++s)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], q[s], sacc, 0, 0, 0);
+      for (int s = 0; s < 16; ++s) {
+        if (s < 4)
+          sacc = mfma16_rot<ROT16>(kf[s], q[s], sacc);
+        else
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], q[s], sacc, 0, 0, 0);
+      }
       // C layout: reg e = key 16w + 4 gq + e, column = head hcol
       float sv[4];
       float mx = -INFINITY;
@@ -172,8 +195,9 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(DecodeArgs da) {
       const bool need = tmax > m_used + kTau;
       if (__ballot(need)) {
         const float m_new = need ? tmax : m_used;
-        const float alpha = exp2f(m_used - m_new);
+        const float alpha = need ? exp2f(m_used - m_new) : 1.0f;
         l_part *= alpha;
+        w_part *= alpha;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
         m_used = m_new;
@@ -184,6 +208,7 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(DecodeArgs da) {
         const float p = sv[e] == -INFINITY ? 0.0f : exp2f(sv[e] - m_used);
         l_part += p;
         pv[e] = (bf16)p;
+        w_part += (float)pv[e];
       }
       *(bf16x4*)(pbuf + hcol * kTile + 16 * w + 4 * gq) = pv;
       __syncthreads();
@@ -213,14 +238,20 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(DecodeArgs da) {
     }
 
     // ---- combine the row sums of the 4 waves and store the partial ----------------------------
-    float ls = l_part;
+    float ls = l_part, ws = w_part;
     ls += __shfl_xor(ls, 16, 64);
     ls += __shfl_xor(ls, 32, 64);
-    if (gq == 0) ssum[w][hcol] = ls;
+    ws += __shfl_xor(ws, 16, 64);
+    ws += __shfl_xor(ws, 32, 64);
+    if (gq == 0) {
+      ssum[w][hcol] = ls;
+      wsum[w][hcol] = ws;
+    }
     __syncthreads();
     const float l_tot = (ssum[0][hcol] + ssum[1][hcol]) + (ssum[2][hcol] + ssum[3][hcol]);
-    const bool nonempty = l_tot > 0.0f;
-    const float inv = nonempty ? 1.0f / l_tot : 0.0f;
+    const float w_tot = (wsum[0][hcol] + wsum[1][hcol]) + (wsum[2][hcol] + wsum[3][hcol]);
+    const bool nonempty = l_tot > 0.0f && w_tot > 0.0f;
+    const float inv = nonempty ? 1.0f / w_tot : 0.0f;
     if (head_ok) {
       float* orow = da.o_part + ((int64_t)slot * rows * a.Hq + rowhead) * kD + 128 * w + 4 * gq;
 #pragma unroll
@@ -237,10 +268,15 @@ hipError_t launch_attn_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.base.B * a.base.T;
   if (rows <= 0 || a.n_spans <= 0) return hipSuccess;
   dim3 grid((unsigned)a.n_spans, (unsigned)(rows * a.base.Hkv)), block(256);
-  if (a.rot_lo)
-    hipLaunchKernelGGL(attn_decode_kernel<true>, grid, block, 0, stream, a);
+  const bool r16 = a.base.rot_f16 != 0;
+  if (a.rot_lo && r16)
+    hipLaunchKernelGGL((attn_decode_kernel<true, true>), grid, block, 0, stream, a);
+  else if (a.rot_lo)
+    hipLaunchKernelGGL((attn_decode_kernel<true, false>), grid, block, 0, stream, a);
+  else if (r16)
+    hipLaunchKernelGGL((attn_decode_kernel<false, true>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL(attn_decode_kernel<false>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_decode_kernel<false, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

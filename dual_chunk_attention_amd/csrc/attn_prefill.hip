@@ -1,4 +1,4 @@
-// Regime flash-attention passes for bf16 prefill on gfx950 (MFMA 32x32x16 bf16).
+// Regime flash-attention passes for bf16 prefill on gfx950 (MFMA 32x32x16).
 //
 // What it computes (DCA feature page, "DCA algorithm" and "Implementation progress +
 // Section-D simplification"): for every query row and each requested regime r, the softmax
@@ -12,20 +12,24 @@
 //  * The 128 rows of a workgroup are QB = 128/G query positions x the G query heads that share
 //    KV head g (GQA), so every K tile staged in LDS serves all of them.  Wave w owns rows
 //    [32w, 32w+32); lane l owns row l%32 in both halves of the wave.
-//  * Scores are computed transposed, S^T = K Q^T: K is the MFMA A operand (read from LDS),
-//    Q^T the B operand (kept in 128 VGPRs for the whole pass).  In the 32x32 result layout a
-//    lane holds 16 keys of its own row, so the row max/sum needs one cross-half exchange.
+//  * Scores are computed transposed, S^T = K Q^T: K is the MFMA A operand (read from LDS), Q^T
+//    the B operand, kept in 128 VGPRs for the whole pass.  In the 32x32 result layout a lane
+//    holds 16 keys of its own row, so the row max/sum needs one cross-half exchange.
 //  * O^T = V^T P^T: the score registers, converted to bf16, are already the B operand (the key
-//    order inside the MFMA k-slots is permuted identically on both operands); V^T fragments are
-//    read from the key-major K tile with the LDS transpose read.  O (512 x 32 per wave) stays in
-//    256 accumulation registers.
+//    order inside the MFMA k-slots is permuted identically on both operands); V^T fragments come
+//    from the key-major K tile through the LDS transpose read.  O (512 x 32 per wave) lives in
+//    the 256 accumulation registers.
+//  * The rotary dims of q_r and k_rot may be fp16 (ROT16): their MFMA k-steps then use the fp16
+//    instruction, whose 11-bit mantissa keeps the rounding of rotated operands 8x below bf16's.
 //  * K tiles of 32 keys are staged by direct global->LDS 16-byte loads into a double buffer:
 //    kqk[32][512] holds rotated dims 0..127 and raw dims 128..511 (QK operand), vlo[32][128]
 //    holds raw dims 0..127 (the rest of the V operand).  16-byte chunks are XOR-swizzled per row
 //    so that both the 8-row b128 reads and the 4-row transpose reads hit distinct banks.
-//  * Online softmax in the log2 domain with a lazy rescale: the running maximum is only moved
-//    when a tile exceeds it by more than 8 (so exp2 arguments stay <= 8 and P fits bf16), which
-//    keeps the 256-register O rescale off the common path.
+//  * Online softmax in the log2 domain against a per-row reference maximum: the first tile with a
+//    valid key sets it, and it only moves when a later tile exceeds it by more than 64 (so exp2
+//    arguments stay <= 64, P and the fp32 sums cannot overflow).  A move flushes the wave's
+//    accumulated O into its own fp32 output rows (rescaled) and restarts O from zero, so O is
+//    never rescaled inside the 256 accumulation registers; the epilogue adds the flushed part.
 //  * Workgroups are launched latest query block first (longest causal work first).
 #include "common.h"
 
@@ -38,7 +42,7 @@ constexpr int kNK = 32;                          // keys per tile
 constexpr int kKqkBytes = kNK * kD * 2;          // 32 KiB
 constexpr int kVloBytes = kNK * kRot * 2;        // 8 KiB
 constexpr int kStageBytes = kKqkBytes + kVloBytes;
-constexpr float kTau = 8.0f;                     // lazy-rescale threshold (log2 units)
+constexpr float kTau = 64.0f;                    // reference-move threshold (log2 units)
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -49,7 +53,21 @@ __device__ __forceinline__ void dma16(const void* src, char* lds_row_base) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_row_base, 16, 0, 0);
 }
 
-template <int G>
+// scheduling-group masks of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+template <bool ROT16>
+__device__ __forceinline__ f32x16 mfma_rot(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  if constexpr (ROT16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+}
+
+template <int G, bool ROT16>
 __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_qblocks) {
   constexpr int QB = 128 / G;  // query positions per workgroup
   __shared__ __attribute__((aligned(1024))) char smem[2 * kStageBytes];
@@ -64,9 +82,9 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
   const int64_t rows = (int64_t)a.B * a.T;
   const float scale_log2 = a.scale * kLog2e;
 
-  // ---- per-position intervals of the three regimes -------------------------------------
-  if (tid < 3 * QB) {
-    const int r = tid / QB, p = tid % QB;
+  // ---- per-position intervals of the three regimes ---------------------------------------
+  for (int e = tid; e < 3 * QB; e += 256) {
+    const int r = e / QB, p = e % QB;
     const int t = qb * QB + p;
     int lo = 0, hi = -1;
     if (t < a.T) {
@@ -77,7 +95,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
     s_hi[r][p] = hi;
   }
 
-  // ---- this lane's query row ----------------------------------------------------------------
+  // ---- this lane's query row -----------------------------------------------------------------
   const int rho = 32 * w + n;
   const int pos_in_blk = rho / G, hh = rho % G;
   const int t = qb * QB + pos_in_blk;
@@ -111,7 +129,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
 
   const int64_t kv_stride = (int64_t)a.Hkv;
   const bf16* kraw_b = (const bf16*)a.k_raw + ((int64_t)b * a.n_kv * kv_stride + g) * kD;
-  const bf16* krot_b = (const bf16*)a.k_rot + ((int64_t)b * a.n_kv * kv_stride + g) * a.k_rot_hs;
+  const char* krot_b = (const char*)a.k_rot + ((int64_t)b * a.n_kv * kv_stride + g) * a.k_rot_hs * 2;
 
   for (int r = 0; r < 3; ++r) {
     if (!a.o[r]) continue;
@@ -136,30 +154,37 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
     f32x16 o[16];
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt) o[dt] = f32x16{};
-    float m_used = -INFINITY, l_part = 0.0f;
+    // l_part: sum of the exact p (for the LSE); w_part: sum of the bf16-rounded p that the PV
+    // product uses (O is normalised by it, so a dominant key's value comes out exactly)
+    float m_used = -INFINITY, l_part = 0.0f, w_part = 0.0f;
+    bool flushed = false;
 
     if (umin <= umax) {
-      const int kt0 = umin / kNK, kt1 = umax / kNK;
+      const int kt0 = max(umin, 0) / kNK, kt1 = min(umax, a.n_kv - 1) / kNK;
+      // K tile k0..k0+31: per-lane byte offsets from a wave-uniform tile base (keys past the
+      // cache end are clamped to the last key; their scores are masked)
+      const int64_t krow_bytes = (int64_t)kv_stride * kD * 2, rrow_bytes = (int64_t)kv_stride * a.k_rot_hs * 2;
       auto issue = [&](int buf, int k0) {
         char* kqk = smem + buf * kStageBytes;
         char* vlo = kqk + kKqkBytes;
+        const char* raw_t = (const char*)kraw_b + (int64_t)k0 * krow_bytes;
+        const char* rot_t = krot_b + (int64_t)k0 * rrow_bytes;
+        const int last = a.n_kv - 1 - k0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int row = 8 * w + i;
-          int key = k0 + row;
-          key = key < a.n_kv ? key : a.n_kv - 1;
+          const int rr = min(row, last);
           const int c = l ^ swz(row & 7);
-          const bf16* src = c < 16 ? krot_b + (int64_t)key * kv_stride * a.k_rot_hs + 8 * c
-                                   : kraw_b + (int64_t)key * kv_stride * kD + 8 * c;
+          const char* src = c < 16 ? rot_t + (uint32_t)(rr * (int)rrow_bytes + 16 * c)
+                                   : raw_t + (uint32_t)(rr * (int)krow_bytes + 16 * c);
           dma16(src, kqk + row * 1024);
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int row = 8 * w + 4 * i + (l >> 4);
-          int key = k0 + row;
-          key = key < a.n_kv ? key : a.n_kv - 1;
+          const int rr = min(row, last);
           const int c = (l & 15) ^ swz(row & 7);
-          dma16(kraw_b + (int64_t)key * kv_stride * kD + 8 * c, vlo + (8 * w + 4 * i) * 256);
+          dma16(raw_t + (uint32_t)(rr * (int)krow_bytes + 16 * c), vlo + (8 * w + 4 * i) * 256);
         }
       };
 
@@ -174,60 +199,94 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
         const char* kqk = smem + cur * kStageBytes;
         const char* vlo = kqk + kKqkBytes;
 
-        // S^T = K Q^T over all 512 dims
+        // ---- S^T = K Q^T over all 512 dims, LDS reads two steps ahead of the MFMAs --------
         f32x16 sacc = f32x16{};
+        {
+          bf16x8 kf[32];
+          kf[0] = *(const bf16x8*)(kqk + qk_off[0]);
+          kf[1] = *(const bf16x8*)(kqk + qk_off[1]);
 #pragma unroll
-        for (int s = 0; s < 32; ++s) {
-          const bf16x8 kf = *(const bf16x8*)(kqk + qk_off[s & 3] + 128 * (s >> 2));
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, q[s], sacc, 0, 0, 0);
-        }
-        const bool full = fmax_lo <= k0 && k0 + kNK - 1 <= fmin_hi;
-        float sv[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          sv[e] = sacc[e] * scale_log2;
-          if (!full) {
-            const int key = k0 + 8 * (e >> 2) + 4 * half + (e & 3);
-            if (key < my_lo || key > my_hi) sv[e] = -INFINITY;
+          for (int s = 0; s < 32; ++s) {
+            if (s + 2 < 32) kf[s + 2] = *(const bf16x8*)(kqk + qk_off[(s + 2) & 3] + 128 * ((s + 2) >> 2));
+            if (s < 8)
+              sacc = mfma_rot<ROT16>(kf[s], q[s], sacc);
+            else
+              sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], q[s], sacc, 0, 0, 0);
+            if (s + 2 < 32) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
           }
         }
-        float mx = sv[0];
+        // ---- mask, row max, lazy rescale, probabilities --------------------------------------
+        const bool full = fmax_lo <= k0 && k0 + kNK - 1 <= fmin_hi;
+        const int lo_eff = full ? -0x7fffffff : my_lo - k0;
+        const int hi_eff = full ? 0x7fffffff : my_hi - k0;
+        float sv[16];
+        float mx = -INFINITY;
 #pragma unroll
-        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sv[e]);
+        for (int e = 0; e < 16; ++e) {
+          const int kk = 8 * (e >> 2) + 4 * half + (e & 3);
+          const bool ok = kk >= lo_eff && kk <= hi_eff;
+          sv[e] = ok ? sacc[e] * scale_log2 : -INFINITY;
+          mx = fmaxf(mx, sv[e]);
+        }
         {
           auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                       false, false);
           mx = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1]));
         }
+        // first valid key of a row: take its tile maximum as the reference (O is still 0)
+        if (m_used == -INFINITY) m_used = mx;
+        // a later tile exceeding the reference by more than kTau: move the accumulated state of
+        // the wave's rows into their fp32 output rows (rescaled to the new reference) and
+        // restart O from zero; with kTau = 64 this is practically never taken
         const bool need = mx > m_used + kTau;
         if (__ballot(need)) {
           const float m_new = need ? mx : m_used;
           const float alpha = exp2f(m_used - m_new);
-          l_part *= alpha;
+          if (row_valid && m_used != -INFINITY) {
+            float* orow = a.o[r] + rowhead * kD + 4 * half;
 #pragma unroll
-          for (int dt = 0; dt < 16; ++dt) o[dt] *= alpha;
+            for (int dt = 0; dt < 16; ++dt) {
+#pragma unroll
+              for (int q4 = 0; q4 < 4; ++q4) {
+                f32x4 v;
+                v[0] = o[dt][4 * q4 + 0];
+                v[1] = o[dt][4 * q4 + 1];
+                v[2] = o[dt][4 * q4 + 2];
+                v[3] = o[dt][4 * q4 + 3];
+                f32x4* dst = (f32x4*)(orow + 32 * dt + 8 * q4);
+                if (flushed) v += *dst;
+                *dst = v * alpha;
+              }
+            }
+            flushed = true;
+          }
+#pragma unroll
+          for (int dt = 0; dt < 16; ++dt) o[dt] = f32x16{};
+          l_part *= alpha;
+          w_part *= alpha;
           m_used = m_new;
         }
-        float p[16];
-        float psum = 0.0f;
+        bf16x8 pk[2];
+        float psum = 0.0f, wsum = 0.0f;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          p[e] = sv[e] == -INFINITY ? 0.0f : exp2f(sv[e] - m_used);
-          psum += p[e];
+          // a masked score is -inf and gives 0; a row without any valid key so far has
+          // m_used = -inf and only masked scores, which must also give 0 (not exp2(NaN))
+          const float p = sv[e] == -INFINITY ? 0.0f : exp2f(sv[e] - m_used);
+          const bf16 pb = (bf16)p;
+          psum += p;
+          wsum += (float)pb;
+          pk[e >> 3][e & 7] = pb;
         }
         l_part += psum;
-        bf16x8 pk0, pk1;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pk0[e] = (bf16)p[e];
-          pk1[e] = (bf16)p[8 + e];
-        }
-        // O^T += V^T P^T
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 pb = ks ? pk1 : pk0;
-#pragma unroll
-          for (int dt = 0; dt < 16; ++dt) {
+        w_part += wsum;
+
+        // ---- O^T += V^T P^T, transpose reads two steps ahead of the MFMAs --------------------
+        {
+          bf16x8 vf[32];
+          auto vload = [&](int i) {
+            const int ks = i >> 4, dt = i & 15;
             const bool lo_part = dt < 4;
             const char* base = lo_part ? vlo : kqk;
             const int stride = lo_part ? 256 : 1024;
@@ -237,10 +296,19 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
                 (lds_bf16x4*)(base + off + (16 * ks) * stride));
             const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                 (lds_bf16x4*)(base + off + (16 * ks + 8) * stride));
-            bf16x8 vf;
-            vf[0] = v0[0]; vf[1] = v0[1]; vf[2] = v0[2]; vf[3] = v0[3];
-            vf[4] = v1[0]; vf[5] = v1[1]; vf[6] = v1[2]; vf[7] = v1[3];
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o[dt], 0, 0, 0);
+            bf16x8 vv;
+            vv[0] = v0[0]; vv[1] = v0[1]; vv[2] = v0[2]; vv[3] = v0[3];
+            vv[4] = v1[0]; vv[5] = v1[1]; vv[6] = v1[2]; vv[7] = v1[3];
+            return vv;
+          };
+          vf[0] = vload(0);
+          vf[1] = vload(1);
+#pragma unroll
+          for (int i = 0; i < 32; ++i) {
+            if (i + 2 < 32) vf[i + 2] = vload(i + 2);
+            o[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pk[i >> 4], o[i & 15], 0, 0, 0);
+            if (i + 2 < 32) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
           }
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -249,14 +317,17 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
     }
 
     // ---- epilogue: normalise and store this regime's partial --------------------------------
-    float l_tot;
+    float l_tot, w_tot;
     {
       auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part),
                                                   false, false);
       l_tot = __uint_as_float(sw2[0]) + __uint_as_float(sw2[1]);
+      auto sw3 = __builtin_amdgcn_permlane32_swap(__float_as_uint(w_part), __float_as_uint(w_part),
+                                                  false, false);
+      w_tot = __uint_as_float(sw3[0]) + __uint_as_float(sw3[1]);
     }
-    const bool nonempty = l_tot > 0.0f;
-    const float inv = nonempty ? 1.0f / l_tot : 0.0f;
+    const bool nonempty = l_tot > 0.0f && w_tot > 0.0f;
+    const float inv = nonempty ? 1.0f / w_tot : 0.0f;
     if (row_valid) {
       float* orow = a.o[r] + rowhead * kD + 4 * half;
 #pragma unroll
@@ -264,11 +335,13 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           f32x4 v;
-          v[0] = o[dt][4 * q4 + 0] * inv;
-          v[1] = o[dt][4 * q4 + 1] * inv;
-          v[2] = o[dt][4 * q4 + 2] * inv;
-          v[3] = o[dt][4 * q4 + 3] * inv;
-          *(f32x4*)(orow + 32 * dt + 8 * q4) = v;
+          v[0] = o[dt][4 * q4 + 0];
+          v[1] = o[dt][4 * q4 + 1];
+          v[2] = o[dt][4 * q4 + 2];
+          v[3] = o[dt][4 * q4 + 3];
+          f32x4* dst = (f32x4*)(orow + 32 * dt + 8 * q4);
+          if (flushed) v += *dst;
+          *dst = v * inv;
         }
       }
       if (half == 0)
@@ -277,9 +350,8 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
   }
 }
 
-}  // namespace
-
-hipError_t launch_attn_prefill_bf16(const AttnArgs& a, hipStream_t stream) {
+template <bool ROT16>
+hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
   const int QB = 128 / G;
   const int n_qblocks = (a.T + QB - 1) / QB;
@@ -287,15 +359,20 @@ hipError_t launch_attn_prefill_bf16(const AttnArgs& a, hipStream_t stream) {
   if (blocks <= 0) return hipSuccess;
   dim3 grid((unsigned)blocks), block(256);
   switch (G) {
-    case 1: hipLaunchKernelGGL(attn_prefill_kernel<1>, grid, block, 0, stream, a, n_qblocks); break;
-    case 2: hipLaunchKernelGGL(attn_prefill_kernel<2>, grid, block, 0, stream, a, n_qblocks); break;
-    case 4: hipLaunchKernelGGL(attn_prefill_kernel<4>, grid, block, 0, stream, a, n_qblocks); break;
-    case 8: hipLaunchKernelGGL(attn_prefill_kernel<8>, grid, block, 0, stream, a, n_qblocks); break;
-    case 16: hipLaunchKernelGGL(attn_prefill_kernel<16>, grid, block, 0, stream, a, n_qblocks); break;
-    case 32: hipLaunchKernelGGL(attn_prefill_kernel<32>, grid, block, 0, stream, a, n_qblocks); break;
+    case 1: hipLaunchKernelGGL((attn_prefill_kernel<1, ROT16>), grid, block, 0, stream, a, n_qblocks); break;
+    case 2: hipLaunchKernelGGL((attn_prefill_kernel<2, ROT16>), grid, block, 0, stream, a, n_qblocks); break;
+    case 4: hipLaunchKernelGGL((attn_prefill_kernel<4, ROT16>), grid, block, 0, stream, a, n_qblocks); break;
+    case 8: hipLaunchKernelGGL((attn_prefill_kernel<8, ROT16>), grid, block, 0, stream, a, n_qblocks); break;
+    case 16: hipLaunchKernelGGL((attn_prefill_kernel<16, ROT16>), grid, block, 0, stream, a, n_qblocks); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_prefill_bf16(const AttnArgs& a, hipStream_t stream) {
+  return a.rot_f16 ? launch_prefill<true>(a, stream) : launch_prefill<false>(a, stream);
 }
 
 }  // namespace dca

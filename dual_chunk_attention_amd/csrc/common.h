@@ -6,6 +6,8 @@
 namespace dca {
 
 typedef __bf16 bf16;
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -21,6 +23,7 @@ __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
+template <> __device__ __forceinline__ f16 from_f32<f16>(float x) { return (f16)x; }     // RNE
 
 __device__ __forceinline__ int64_t floordiv64(int64_t a, int64_t b) {
   int64_t q = a / b;
@@ -60,7 +63,8 @@ struct RopeArgs {
   int32_t chunk;
   int64_t rows;
   int32_t n_heads, n_rot, head_dim;
-  int32_t copy_tail;        // copy dims [n_rot, head_dim) as well
+  int32_t copy_tail;        // copy dims [n_rot, head_dim) as well (same in/out type only)
+  int32_t out_f16;          // bf16 input written as fp16 (the rotated operands of the bf16 path)
   int32_t planes;
   double theta;
   const float* freq_factors;  // [n_rot/2] or NULL
@@ -106,6 +110,7 @@ struct AttnArgs {
   float* lse[3];
   int32_t B, T, Hq, Hkv, n_kv, D, n_rot;
   float scale;
+  int32_t rot_f16;           // bf16 path: q_rot / k_rot rotary dims are fp16 (else bf16)
 };
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
 

@@ -11,7 +11,7 @@ namespace {
 
 constexpr int kRopeRows = 4;   // rows per block
 
-template <typename T>
+template <typename T, typename TO>
 __global__ __launch_bounds__(256) void rope_kernel(RopeArgs a) {
   __shared__ double w_s[512];
   const int half = a.n_rot / 2;
@@ -23,7 +23,7 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeArgs a) {
   __syncthreads();
   const int z = blockIdx.z;
   const T* __restrict__ x = (const T*)a.x;
-  T* __restrict__ y = (T*)a.y + (int64_t)z * a.y_plane_stride;
+  TO* __restrict__ y = (TO*)a.y + (int64_t)z * a.y_plane_stride;
   const int64_t row0 = (int64_t)blockIdx.x * kRopeRows;
   const int n = kRopeRows * half;
   for (int e = threadIdx.x; e < n; e += blockDim.x) {
@@ -41,14 +41,14 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeArgs a) {
     const float cs = (float)cd, sn = (float)sd;
     for (int h = 0; h < a.n_heads; ++h) {
       const T* xr = x + row * a.x_row_stride + (int64_t)h * a.x_head_stride;
-      T* yr = y + row * a.y_row_stride + (int64_t)h * a.y_head_stride;
+      TO* yr = y + row * a.y_row_stride + (int64_t)h * a.y_head_stride;
       const float x0 = to_f32(xr[f]);
       const float x1 = to_f32(xr[f + half]);
-      yr[f] = from_f32<T>(fmaf(x0, cs, -x1 * sn));
-      yr[f + half] = from_f32<T>(fmaf(x0, sn, x1 * cs));
+      yr[f] = from_f32<TO>(fmaf(x0, cs, -x1 * sn));
+      yr[f + half] = from_f32<TO>(fmaf(x0, sn, x1 * cs));
     }
   }
-  if (a.copy_tail) {
+  if (a.copy_tail && sizeof(T) == sizeof(TO)) {
     const int tail = a.head_dim - a.n_rot;
     const int m = kRopeRows * a.n_heads * tail;
     for (int e = threadIdx.x; e < m; e += blockDim.x) {
@@ -56,8 +56,8 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeArgs a) {
       const int rem = e % (a.n_heads * tail);
       const int h = rem / tail, d = a.n_rot + rem % tail;
       if (row >= a.rows) continue;
-      y[row * a.y_row_stride + (int64_t)h * a.y_head_stride + d] =
-          x[row * a.x_row_stride + (int64_t)h * a.x_head_stride + d];
+      const T v = x[row * a.x_row_stride + (int64_t)h * a.x_head_stride + d];
+      y[row * a.y_row_stride + (int64_t)h * a.y_head_stride + d] = *(const TO*)&v;
     }
   }
 }
@@ -86,10 +86,12 @@ __global__ void rope_tables_kernel(float2* lo, float2* hi, int32_t n_hi, int32_t
 hipError_t launch_rope(const RopeArgs& a, bool bf16_data, hipStream_t stream) {
   if (a.rows <= 0 || a.planes <= 0) return hipSuccess;
   dim3 grid((unsigned)((a.rows + kRopeRows - 1) / kRopeRows), 1, (unsigned)a.planes);
-  if (bf16_data)
-    hipLaunchKernelGGL(rope_kernel<bf16>, grid, dim3(256), 0, stream, a);
+  if (bf16_data && a.out_f16)
+    hipLaunchKernelGGL((rope_kernel<bf16, f16>), grid, dim3(256), 0, stream, a);
+  else if (bf16_data)
+    hipLaunchKernelGGL((rope_kernel<bf16, bf16>), grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(rope_kernel<float>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((rope_kernel<float, float>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -59,6 +59,8 @@ def lib():
                                     vp, vp, sz, vp]
         L.dca_attention_workspace_size.argtypes = [cfgp, ctypes.c_int, i32, i32, i32]
         L.dca_attention_workspace_size.restype = sz
+        L.dca_set_stage_events.argtypes = [vp, i32]
+        L.dca_set_stage_events.restype = ctypes.c_int
         L.dca_last_error.restype = ctypes.c_char_p
         for f in ("dca_remap_positions", "dca_rope_partial", "dca_attn_regime", "dca_lse_merge",
                   "dca_attention"):
@@ -202,3 +204,16 @@ def attention(cfg: Config, q: torch.Tensor, q_pos: torch.Tensor, k: torch.Tensor
                                _dtype_code(od), _ptr(out), _ptr(lse), _ptr(workspace),
                                workspace.numel(), _stream()))
     return out, lse
+
+
+N_STAGE_EVENTS = 6
+
+
+def set_stage_events(events_array) -> None:
+    """dca_set_stage_events: `events_array` is a ctypes array of >= 6 hipEvent_t handles created by
+    the caller (None turns the hook off).  Later dca_attention calls on this thread record them
+    around their stages."""
+    if events_array is None:
+        _check(lib().dca_set_stage_events(None, 0))
+    else:
+        _check(lib().dca_set_stage_events(ctypes.cast(events_array, ctypes.c_void_p), len(events_array)))

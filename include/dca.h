@@ -152,6 +152,15 @@ dca_status dca_attention(const dca_config* cfg, dca_dtype dtype, int32_t B, int3
 size_t dca_attention_workspace_size(const dca_config* cfg, dca_dtype dtype, int32_t B, int32_t T,
                                     int32_t n_kv);
 
+/* Optional stage timing for dca_attention (measurement hook; no page defines it).  After
+ * dca_set_stage_events(ev, n) with n >= DCA_N_STAGE_EVENTS, every dca_attention call made later on
+ * this thread records, on its stream: ev[0] before the remap, ev[1] after the remap, ev[2] after
+ * the query rotation, ev[3] after the key rotation (prefill) or the cos/sin tables (decode), ev[4]
+ * after the regime passes, ev[5] after the merge.  The events are created and owned by the caller
+ * (hipEventCreate); NULL or n = 0 turns the hook off.  n in (0, DCA_N_STAGE_EVENTS) is an error. */
+#define DCA_N_STAGE_EVENTS 6
+dca_status dca_set_stage_events(hipEvent_t* events, int32_t n);
+
 /* Thread-local text describing the last non-OK status returned on this thread ("" if none). */
 const char* dca_last_error(void);
 

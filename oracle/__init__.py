@@ -42,7 +42,7 @@ def _lib():
         lib.dca_oracle_attention.restype = ctypes.c_int
         lib.dca_oracle_attention.argtypes = [
             i64, i64, i64, i64, i64, ctypes.c_double, ctypes.c_double, f64p, ctypes.c_int,
-            i64, i64, ctypes.c_void_p, i32p, ctypes.c_void_p, i64, i64,
+            ctypes.c_int, i64, i64, ctypes.c_void_p, i32p, ctypes.c_void_p, i64, i64,
             ctypes.POINTER(ctypes.c_int64), f64p, f64p, f64p, f64p, ctypes.c_int]
         _LIB = lib
     return _LIB
@@ -113,11 +113,13 @@ def merge(o_parts, lse_parts):
 
 
 def attention(q, qpos, k, *, chunk, n_rot, theta, scale, freq_factors=None, rows=None,
-              per_regime=True, n_threads=0):
+              per_regime=True, n_threads=0, round_rotated_bf16=False):
     """DCA attention of selected query rows in fp64.
 
     q [B, T, Hq, D] and k [B, N, Hkv, D] are float32 arrays or uint16 bf16 bit patterns (same
     kind for both); qpos int32 [B, T]; rows = flat row indices b*T+t (default: all).
+    round_rotated_bf16: round the rotated dims of queries and keys to bf16 before the scores
+    (the contract of a caller passing bf16 rotated operands to the per-regime entry point).
     Returns dict(o [n, Hq, D], lse [n, Hq], o_reg [3, n, Hq, D], lse_reg [3, n, Hq], rows)."""
     q = np.ascontiguousarray(q)
     k = np.ascontiguousarray(k)
@@ -140,7 +142,7 @@ def attention(q, qpos, k, *, chunk, n_rot, theta, scale, freq_factors=None, rows
     ff = None if freq_factors is None else np.ascontiguousarray(freq_factors, dtype=np.float64)
     st = _lib().dca_oracle_attention(
         D, int(n_rot), Hq, Hkv, int(chunk), float(theta), float(scale),
-        None if ff is None else _ptr(ff, ctypes.c_double), in_bf16, B, T,
+        None if ff is None else _ptr(ff, ctypes.c_double), in_bf16, 1 if round_rotated_bf16 else 0, B, T,
         q.ctypes.data_as(ctypes.c_void_p), _ptr(qpos, ctypes.c_int32),
         k.ctypes.data_as(ctypes.c_void_p), N, n, _ptr(sel, ctypes.c_int64),
         _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double),

@@ -168,6 +168,17 @@ static double load_in(const void* p, int64_t e, int in_bf16) {
   return (double)((const float*)p)[e];
 }
 
+/* Round-to-nearest-even of a double to bf16 (through fp32, as a rotated value is formed in fp32
+ * and then stored as bf16), returned as a double. */
+static double round_bf16(double v) {
+  float f = (float)v;
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  u = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
 /* N-way LSE merge ([F] "Implementation progress + Section-D simplification"; zero weight of an
  * empty part from "Section C2b"; zero exp-sum rule from [U] entry 0110).
  * o_parts [n_parts][rows][D], lse_parts [n_parts][rows] -> o [rows][D], lse [rows]. */
@@ -197,9 +208,13 @@ void dca_oracle_merge(int64_t n_parts, const double* o_parts, const double* lse_
  *   sel  [n_sel] flat row indices b*T + t
  *   o    [n_sel][Hq][D],  lse [n_sel][Hq]                    -- union softmax (the definition)
  *   o_reg [3][n_sel][Hq][D], lse_reg [3][n_sel][Hq] (NULL ok) -- per-regime partials
+ * rot_round = 1 rounds the rotated dims of the queries and keys to bf16 (nearest-even) before
+ * the scores are formed: the contract of a caller that hands over bf16 rotated operands (used to
+ * check the per-regime entry point); 0 keeps them exact.
  * Returns 0, or -1 on allocation failure, -2 on a bad argument. */
 int dca_oracle_attention(int64_t D, int64_t n_rot, int64_t Hq, int64_t Hkv, int64_t c,
-                         double theta, double scale, const double* ff, int in_bf16, int64_t B,
+                         double theta, double scale, const double* ff, int in_bf16, int rot_round,
+                         int64_t B,
                          int64_t T, const void* q, const int32_t* qpos, const void* k, int64_t n_kv,
                          int64_t n_sel, const int64_t* sel, double* o, double* lse, double* o_reg,
                          double* lse_reg, int n_threads) {
@@ -229,6 +244,8 @@ int dca_oracle_attention(int64_t D, int64_t n_rot, int64_t Hq, int64_t Hkv, int6
         for (int64_t d = 0; d < n_rot; ++d)
           xin[d] = load_in(k, ((b * n_kv + j) * Hkv + g) * D + d, in_bf16);
         rope_one(n_rot, n_rot, theta, ff, xin, (double)dca_oracle_key_pos(j, c), xout);
+        if (rot_round == 1)
+          for (int64_t d = 0; d < n_rot; ++d) xout[d] = round_bf16(xout[d]);
         memcpy(krot + (j * Hkv + g) * n_rot, xout, sizeof(double) * n_rot);
       }
     }
@@ -252,8 +269,11 @@ int dca_oracle_attention(int64_t D, int64_t n_rot, int64_t Hq, int64_t Hkv, int6
           int64_t i = qpos[flat];
           int64_t g = h / G;
           for (int64_t d = 0; d < D; ++d) qv[d] = load_in(q, (flat * Hq + h) * D + d, in_bf16);
-          for (int r = 0; r < 3; ++r)
+          for (int r = 0; r < 3; ++r) {
             rope_one(n_rot, D, theta, ff, qv, (double)dca_oracle_query_pos(i, c, r), qr + r * D);
+            if (rot_round == 1)
+              for (int64_t d = 0; d < n_rot; ++d) qr[r * D + d] = round_bf16(qr[r * D + d]);
+          }
           int64_t jmax = i < n_kv - 1 ? i : n_kv - 1;
           /* scores of every attended key, each with its own regime's query rotation */
           for (int64_t j = 0; j <= jmax; ++j) {

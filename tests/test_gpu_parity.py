@@ -22,11 +22,11 @@ def _inputs(w, **kw):
     return inp, w, ff
 
 
-def _oracle_attention(inp, w, rows=None, chunk=None, per_regime=True):
+def _oracle_attention(inp, w, rows=None, chunk=None, per_regime=True, round_rotated_bf16=False):
     ff = inp["freq_factors"].astype(np.float64) if w.ff_uniform else None
     return oracle.attention(inp["q"], inp["q_pos"], inp["k"], chunk=w.chunk if chunk is None else chunk,
                             n_rot=w.n_rot, theta=w.theta, scale=w.scale, freq_factors=ff, rows=rows,
-                            per_regime=per_regime)
+                            per_regime=per_regime, round_rotated_bf16=round_rotated_bf16)
 
 
 # ----------------------------------------------------------------------------------------------
@@ -145,7 +145,9 @@ def test_attn_regime_each_regime(label, name, over, chunk, rows):
     q, k, qp = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["q_pos"])
     pos_q, pos_k, bounds = dca.remap_positions(cfg, qp, N)
     k_rot = dca.rope_partial(cfg, k.reshape(B * N, w.Hkv, w.D), pos_k.repeat(B)).reshape(k.shape)
-    res = _oracle_attention(inp, w, chunk=c)
+    # this entry point receives rotated operands in the data type (bf16 here): the oracle rounds
+    # its own fp64 rotations the same way, so the comparison isolates the attention pass
+    res = _oracle_attention(inp, w, chunk=c, round_rotated_bf16=w.dtype == "bf16")
     for r in range(3):
         q_r = dca.rope_partial(cfg, q.reshape(B * T, w.Hq, w.D), pos_q[r].reshape(-1).contiguous())
         o_r, l_r = dca.attn_regime(cfg, r, q_r.reshape(q.shape), bounds, k_rot, k)
@@ -213,12 +215,13 @@ def _probe_inputs(T, N, q0, seed, kind):
         q[..., 0] = 6.0 * np.sqrt(512)
         k[..., :128] = 0.0
         k[..., 64] = 1.0
-    else:  # needles: a few keys equal to a scaled copy of a query's tail
+    else:  # needles: a few keys equal to the direction of a query's tail (unit RMS)
         for t in rng.integers(0, T, 24):
             i = q0 + t
             for j in {int(i), int(max(0, i - 3)), int(max(0, i - 300)), int(rng.integers(0, i + 1))}:
                 for g in range(2):
-                    k[0, j, g, 128:] = 3.0 * q[0, t, 8 * g + int(rng.integers(0, 8)), 128:] / np.sqrt(np.mean(q[0, t, 0, 128:] ** 2))
+                    qq = q[0, t, 8 * g + int(rng.integers(0, 8)), 128:]
+                    k[0, j, g, 128:] = qq / np.sqrt(np.mean(qq ** 2))   # unit RMS, like every key
     inp["q"], inp["k"] = synth.bf16_bits(q), synth.bf16_bits(k)
     return inp, w
 
@@ -308,4 +311,34 @@ def test_batch_of_prefill_sequences():
     torch.cuda.synchronize()
     res = _oracle_attention(inp, w, per_regime=False)
     assert_o_close(o.cpu().numpy().reshape(-1, 16, 512), res["o"])
+    assert_lse_close(lse.cpu().numpy().reshape(-1, 16), res["lse"])
+
+
+@pytest.mark.parametrize("T,N,q0", [(256, 256, 0), (1, 3000, 2999)])
+def test_reference_move_with_extreme_scores(T, N, q0):
+    """Needle keys whose scores exceed everything seen before by far more than 64 (log2 units)
+    force the prefill kernel to move its per-row reference (flush of O into the output rows) and
+    the decode kernel to rescale; both must still equal the oracle."""
+    w = synth.Workload("extreme", 1, T, q0, N, 64 if T > 1 else 1024, 16, 2, "bf16", 91)
+    inp = synth.make_inputs(w)
+    q = synth.bf16_to_f32(inp["q"]).copy()
+    k = synth.bf16_to_f32(inp["k"]).copy()
+    rng = np.random.default_rng(92)
+    for t in rng.choice(T, min(T, 40), replace=False):
+        i = q0 + int(t)
+        # a mild needle early in the row's range, a huge one later
+        for j, amp in [(max(0, i - int(rng.integers(40, 60))), 4.0), (i - int(rng.integers(0, 3)), 12.0)]:
+            if j < 0:
+                continue
+            h = int(rng.integers(0, 16))
+            qq = q[0, t, h, 128:]
+            k[0, j, h // 8, 128:] = amp * qq / np.sqrt(np.mean(qq ** 2))
+    inp["q"], inp["k"] = synth.bf16_bits(q), synth.bf16_bits(k)
+    ffd = to_dev(inp["freq_factors"])
+    o, lse = dca.attention(cfg_for(w, ffd), to_dev(inp["q"]), to_dev(inp["q_pos"]), to_dev(inp["k"]),
+                           o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    res = _oracle_attention(inp, w, per_regime=False)
+    assert res["lse"].max() > 60.0            # scores really are extreme
+    assert_o_close(o.cpu().numpy().reshape(-1, 16, 512), res["o"], atol=2e-2)
     assert_lse_close(lse.cpu().numpy().reshape(-1, 16), res["lse"])

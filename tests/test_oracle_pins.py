@@ -252,6 +252,43 @@ def test_attention_matches_eager_dense_form(B, T, N, Hq, Hkv, D, q0, c):
     np.testing.assert_allclose(l_m, res["lse"].reshape(-1), rtol=1e-13)
 
 
+def test_attention_bf16_rounded_rotations_match_eager_form():
+    """The rounded-rotation option equals the dense form with rotated q/k rounded by PyTorch's
+    float->bf16 conversion (nearest-even)."""
+    B, T, N, Hq, Hkv, D, q0, c = 1, 29, 29, 2, 1, 16, 0, 4
+    inp = _small_inputs(B, T, N, Hq, Hkv, D, q0, seed=55)
+    q, k, qpos, ff = inp["q"], inp["k"], inp["q_pos"], inp["freq_factors"].astype(np.float64)
+    n_rot, theta, scale = 16, 1.0e6, 0.25
+    res = oracle.attention(q, qpos, k, chunk=c, n_rot=n_rot, theta=theta, scale=scale, freq_factors=ff,
+                           round_rotated_bf16=True)
+
+    def rnd(x):
+        return torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).double().numpy()
+
+    qf, kf = q.astype(np.float64), k.astype(np.float64)
+    G = Hq // Hkv
+    i = qpos.astype(np.int64)[0]
+    j = np.arange(N)
+    S = np.full((T, Hq, N), -np.inf)
+    kr = _rope_complex(kf[0], j % c, n_rot, theta, ff)
+    kr[..., :n_rot] = rnd(kr[..., :n_rot])
+    for r, pq in enumerate([i % c, i % c + c, np.full_like(i, c - 1)]):
+        qr = _rope_complex(qf[0], pq, n_rot, theta, ff)
+        qr[..., :n_rot] = rnd(qr[..., :n_rot])
+        for t in range(T):
+            for h in range(Hq):
+                for jj in range(N):
+                    if oracle.regime(i[t], jj, c, N) == r:
+                        S[t, h, jj] = scale * float(qr[t, h] @ kr[jj, h // G])
+    lse = scipy.special.logsumexp(S, axis=-1)
+    O = np.einsum("thn,nhd->thd", np.exp(S - lse[..., None]), np.repeat(kf[0], G, axis=1))
+    np.testing.assert_allclose(res["lse"], lse, rtol=1e-12)
+    np.testing.assert_allclose(res["o"], O, atol=1e-12)
+    # and the rounding matters at this size (it is not a no-op)
+    ex = oracle.attention(q, qpos, k, chunk=c, n_rot=n_rot, theta=theta, scale=scale, freq_factors=ff)
+    assert np.abs(ex["lse"] - res["lse"]).max() > 1e-6
+
+
 def test_attention_chunk_covers_sequence_equals_sdpa():
     """c >= seqlen collapses DCA to plain causal attention with RoPE at the true positions
     (DCA feature page, flags section and "Section B (gemma4)"); checked against PyTorch's
