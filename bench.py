@@ -12,6 +12,7 @@ query rows of the same workload on the host cores.
 """
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -46,6 +47,19 @@ class HipEvents:
         assert self.hip.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(self.arr[i]),
                                             ctypes.c_void_p(self.arr[j])) == 0
         return float(out.value)
+
+
+def measured_traffic(kernel_file):
+    """HBM bytes per launch of a kernel, from the FETCH_SIZE/WRITE_SIZE counter passes recorded in
+    profiles/traffic.json; None when the kernel source changed since the counters were taken."""
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))[kernel_file]
+        src = open(os.path.join(ROOT, "dual_chunk_attention_amd", "csrc", kernel_file), "rb").read()
+    except (OSError, KeyError, ValueError):
+        return None
+    if hashlib.sha256(src).hexdigest()[:16] != rec.get("sha256_16"):
+        return None
+    return float(rec["bytes"])
 
 
 def to_dev(torch, a):
@@ -123,6 +137,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=96)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (reference for the traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this path has no multi-GPU mode (see DESIGN.md for how it "
@@ -154,7 +170,8 @@ def main():
         "config": {"workload": w.name, "B": w.B, "T": w.T, "n_kv": w.N, "chunk": w.chunk,
                    "heads_q": w.Hq, "heads_kv": w.Hkv, "head_dim": w.D, "n_rot": w.n_rot},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": measured_traffic("attn_prefill.hip") if w.name == "prefill-32k-c8192" else None,
                      "kernel": "attn_prefill_kernel (3 regime passes, one launch)",
                      "kernel_ms": attn_ms, "algorithmic_flop": flops},
         "stages_ms": {"remap": stages[0], "rope_q": stages[1], "rope_k": stages[2],
@@ -171,13 +188,22 @@ def main():
             "workload": wd.name, "value": wd.B * wd.T / (msd * 1e-3), "unit": "tokens/s",
             "ms_per_step": msd, "steps": args.decode_steps,
             "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                         "frac": gbps / HBM_PEAK_GBPS,
+                         "traffic": measured_traffic("attn_decode.hip") if wd.name == "decode-b8-kv256k-c65536" else None,
                          "kernel": "attn_decode_kernel (split-KV, 3 regimes)", "kernel_ms": std[3],
                          "algorithmic_bytes": kv_bytes},
             "stages_ms": {"remap": std[0], "rope_q": std[1], "tables": std[2],
                           "regime_passes": std[3], "merge": std[4]},
         }
         del inpd
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        rec["copy_calibration_bytes"] = int(src.numel() * 4)
+        del src, dst
     if not args.no_cpu_baseline:
         inp = synth.make_inputs(w)
         rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_rows)

@@ -316,29 +316,30 @@ def test_batch_of_prefill_sequences():
 
 @pytest.mark.parametrize("T,N,q0", [(256, 256, 0), (1, 3000, 2999)])
 def test_reference_move_with_extreme_scores(T, N, q0):
-    """Needle keys whose scores exceed everything seen before by far more than 64 (log2 units)
-    force the prefill kernel to move its per-row reference (flush of O into the output rows) and
-    the decode kernel to rescale; both must still equal the oracle."""
+    """Queries scaled by 12 aligned with unit-RMS needle keys: the needle scores exceed everything
+    seen before by far more than 64 (log2 units), which makes the prefill kernel move its per-row
+    reference (flush of O into the output rows) and the decode kernel rescale.  Values stay unit
+    RMS, so the 1e-2 bar applies; LSE is checked at 1e-3."""
     w = synth.Workload("extreme", 1, T, q0, N, 64 if T > 1 else 1024, 16, 2, "bf16", 91)
     inp = synth.make_inputs(w)
     q = synth.bf16_to_f32(inp["q"]).copy()
     k = synth.bf16_to_f32(inp["k"]).copy()
     rng = np.random.default_rng(92)
-    for t in rng.choice(T, min(T, 40), replace=False):
+    rows = [T - 1] if T == 1 else list(range(3, T, 7))      # distinct positions, distinct keys
+    for t in rows:
         i = q0 + int(t)
-        # a mild needle early in the row's range, a huge one later
-        for j, amp in [(max(0, i - int(rng.integers(40, 60))), 4.0), (i - int(rng.integers(0, 3)), 12.0)]:
-            if j < 0:
-                continue
-            h = int(rng.integers(0, 16))
+        for h in range(16):
+            q[0, t, h, 128:] *= 12.0
+        # a later (closer) key aligned with head 3's query, an earlier one with head 11's
+        for j, h in [(i - (t % 3), 3), (max(0, i - 5 - (t % 3)), 11)]:
             qq = q[0, t, h, 128:]
-            k[0, j, h // 8, 128:] = amp * qq / np.sqrt(np.mean(qq ** 2))
+            k[0, j, h // 8, 128:] = qq / np.sqrt(np.mean(qq ** 2))
     inp["q"], inp["k"] = synth.bf16_bits(q), synth.bf16_bits(k)
     ffd = to_dev(inp["freq_factors"])
     o, lse = dca.attention(cfg_for(w, ffd), to_dev(inp["q"]), to_dev(inp["q_pos"]), to_dev(inp["k"]),
                            o_dtype=torch.float32)
     torch.cuda.synchronize()
     res = _oracle_attention(inp, w, per_regime=False)
-    assert res["lse"].max() > 60.0            # scores really are extreme
-    assert_o_close(o.cpu().numpy().reshape(-1, 16, 512), res["o"], atol=2e-2)
+    assert res["lse"].max() > 100.0            # scores really are extreme
+    assert_o_close(o.cpu().numpy().reshape(-1, 16, 512), res["o"])
     assert_lse_close(lse.cpu().numpy().reshape(-1, 16), res["lse"])
