@@ -30,7 +30,9 @@ constexpr float kTau = 8.0f;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// 16-byte chunk swizzle of a tile row, conflict-free on gfx950 (256-byte bank window) for the
+// 16-row b128 reads and the 4-row transpose reads below.
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
 template <bool ROT16>
 __device__ __forceinline__ f32x4 mfma16_rot(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(DecodeArgs da) {
   const int qrow = 16 * w + hcol;
   int qk_off[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) qk_off[u] = qrow * 1024 + 16 * ((4 * u + gq) ^ swz(qrow & 7));
+  for (int u = 0; u < 4; ++u) qk_off[u] = qrow * 1024 + 16 * ((4 * u + gq) ^ swz(qrow));
   // PV operand (transpose read): rows 32 ks + 8 gq + 4 e + j/4, dims 128 w + 16 dt + 4 (j%4).
   const int j16 = l & 15;
 
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(DecodeArgs da) {
         const int row = 16 * w + i;
         int key = k0 + row;
         key = min(max(key, 0), a.n_kv - 1);
-        const int c = l ^ swz(row & 7);
+        const int c = l ^ swz(row);
         __builtin_amdgcn_global_load_lds(kraw_b + (int64_t)key * a.Hkv * kD + 8 * c,
                                          (lds_void*)(base + row * 1024), 16, 0, 0);
       }
@@ -224,7 +226,7 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(DecodeArgs da) {
           for (int e = 0; e < 2; ++e) {
             const int row = 32 * ks + 8 * gq + 4 * e + (j16 >> 2);
             const int c = 16 * w + 2 * dt + ((j16 >> 1) & 1);
-            const int off = row * 1024 + 16 * (c ^ swz(row & 7)) + 8 * (j16 & 1);
+            const int off = row * 1024 + 16 * (c ^ swz(row)) + 8 * (j16 & 1);
             v[e] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(kb + off));
           }
           bf16x8 vf;

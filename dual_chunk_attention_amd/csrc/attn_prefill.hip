@@ -24,7 +24,7 @@
 //  * K tiles of 32 keys are staged by direct global->LDS 16-byte loads into a double buffer:
 //    kqk[32][512] holds rotated dims 0..127 and raw dims 128..511 (QK operand), vlo[32][128]
 //    holds raw dims 0..127 (the rest of the V operand).  16-byte chunks are XOR-swizzled per row
-//    so that both the 8-row b128 reads and the 4-row transpose reads hit distinct banks.
+//    so that both the 16-row b128 reads and the 4-row transpose reads are bank-conflict free.
 //  * Online softmax in the log2 domain against a per-row reference maximum: the first tile with a
 //    valid key sets it, and it only moves when a later tile exceeds it by more than 64 (so exp2
 //    arguments stay <= 64, P and the fp32 sums cannot overflow).  A move flushes the wave's
@@ -47,7 +47,10 @@ constexpr float kTau = 64.0f;                    // reference-move threshold (lo
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// 16-byte chunk swizzle of a tile row (gfx950 LDS conflicts within 256-byte windows): rows
+// r..r+15 map one logical chunk to 16 distinct slots (the 16-lane b128 reads of the QK operand),
+// and rows 4k..4k+3 map a chunk pair to distinct 32-byte slots (the 32-lane transpose reads).
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
 __device__ __forceinline__ void dma16(const void* src, char* lds_row_base) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_row_base, 16, 0, 0);
@@ -110,20 +113,24 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
     for (int s = 8; s < 32; ++s) q[s] = *(const bf16x8*)(qt + 16 * s - kRot);
   }
 
-  // LDS read offsets (bytes).  QK operand: row n, chunk (2s + half) ^ swz(n).
-  int qk_off[4];
+  // LDS read offsets (bytes).  QK operand: row n, chunk c = 2s + half at (c ^ swz(n)):
+  // byte n*1024 + 256*(s>>3) + qk_off[s & 7].
+  int qk_off[8];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) qk_off[u] = n * 1024 + 16 * ((2 * u + half) ^ swz(n & 7));
-  // V^T operand (transpose read): row 4*half + (l%16)/4 (+ 16 ks + 8 e), dims
-  // 32 dt + 16 grp + 4 (j%4); chunk 4 dt + c0 with c0 = 2 grp + (j/2)%2, byte (j%2)*8.
-  const int j16 = l & 15, grp = (l >> 4) & 1;
-  const int rho_l = 4 * half + (j16 >> 2);
-  const int sw = swz(rho_l & 7);
+  for (int u = 0; u < 8; ++u) qk_off[u] = n * 1024 + 16 * ((2 * u + half) ^ swz(n));
+  // V^T operand (transpose read) for k-step ks, dim tile dt, half e of the 8 k-slots:
+  // row 16ks + 8e + 4half + jj (jj = (l%16)/4), dims 32dt + 16grp + 4(l%4), i.e. chunk
+  // 4dt + c0 (c0 = 2grp + (l/2)%2) at byte 8(l%2).  swz(row) = 4jj + (2e + half), so the
+  // swizzled chunk is 4(dt ^ jj) + (c0 ^ (2e + half)).
+  const int j16 = l & 15, grp = (l >> 4) & 1, jj = j16 >> 2;
+  const int rho_l = 4 * half + jj;
   const int c0 = 2 * grp + ((j16 >> 1) & 1);
-  const int b2 = sw >> 2;
-  const int cpart = 16 * (c0 ^ (sw & 3)) + 8 * (j16 & 1);
-  const int v_lo_even = rho_l * 256 + cpart + 64 * b2, v_lo_odd = rho_l * 256 + cpart - 64 * b2;
-  const int v_hi_even = rho_l * 1024 + cpart + 64 * b2, v_hi_odd = rho_l * 1024 + cpart - 64 * b2;
+  int v_e[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) v_e[e] = 16 * (c0 ^ (2 * e + half)) + 8 * (j16 & 1);
+  int v_dt[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) v_dt[u] = 64 * (u ^ jj);
 
   __syncthreads();
 
@@ -161,30 +168,32 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
 
     if (umin <= umax) {
       const int kt0 = max(umin, 0) / kNK, kt1 = min(umax, a.n_kv - 1) / kNK;
-      // K tile k0..k0+31: per-lane byte offsets from a wave-uniform tile base (keys past the
-      // cache end are clamped to the last key; their scores are masked)
+      // K tile k0..k0+31 by direct global->LDS loads.  Row `row` lane l fills physical chunk l
+      // with logical chunk l ^ swz(row); since swz < 16 that is a rotary chunk exactly for lanes
+      // 0..15.  Byte offsets from the tile base are loop-invariant except in the cache's last
+      // tile, where rows past the end re-read the last key (their scores are masked).
       const int64_t krow_bytes = (int64_t)kv_stride * kD * 2, rrow_bytes = (int64_t)kv_stride * a.k_rot_hs * 2;
+      const bool rot_lane = l < 16;
+      const int lane_row_bytes = (int)(rot_lane ? rrow_bytes : krow_bytes);
       auto issue = [&](int buf, int k0) {
         char* kqk = smem + buf * kStageBytes;
         char* vlo = kqk + kKqkBytes;
         const char* raw_t = (const char*)kraw_b + (int64_t)k0 * krow_bytes;
-        const char* rot_t = krot_b + (int64_t)k0 * rrow_bytes;
+        const char* lane_t = rot_lane ? krot_b + (int64_t)k0 * rrow_bytes : raw_t;
         const int last = a.n_kv - 1 - k0;
+        const bool tail = last < kNK - 1;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int row = 8 * w + i;
-          const int rr = min(row, last);
-          const int c = l ^ swz(row & 7);
-          const char* src = c < 16 ? rot_t + (uint32_t)(rr * (int)rrow_bytes + 16 * c)
-                                   : raw_t + (uint32_t)(rr * (int)krow_bytes + 16 * c);
-          dma16(src, kqk + row * 1024);
+          const int rr = tail ? min(row, last) : row;
+          dma16(lane_t + (uint32_t)(rr * lane_row_bytes + 16 * (l ^ swz(row))), kqk + row * 1024);
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int row = 8 * w + 4 * i + (l >> 4);
-          const int rr = min(row, last);
-          const int c = (l & 15) ^ swz(row & 7);
-          dma16(raw_t + (uint32_t)(rr * (int)krow_bytes + 16 * c), vlo + (8 * w + 4 * i) * 256);
+          const int rr = tail ? min(row, last) : row;
+          dma16(raw_t + (uint32_t)(rr * (int)krow_bytes + 16 * ((l & 15) ^ swz(row))),
+                vlo + (8 * w + 4 * i) * 256);
         }
       };
 
@@ -207,7 +216,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
           kf[1] = *(const bf16x8*)(kqk + qk_off[1]);
 #pragma unroll
           for (int s = 0; s < 32; ++s) {
-            if (s + 2 < 32) kf[s + 2] = *(const bf16x8*)(kqk + qk_off[(s + 2) & 3] + 128 * ((s + 2) >> 2));
+            if (s + 2 < 32) kf[s + 2] = *(const bf16x8*)(kqk + qk_off[(s + 2) & 7] + 256 * ((s + 2) >> 3));
             if (s < 8)
               sacc = mfma_rot<ROT16>(kf[s], q[s], sacc);
             else
@@ -217,18 +226,21 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
           }
         }
         // ---- mask, row max, lazy rescale, probabilities --------------------------------------
-        const bool full = fmax_lo <= k0 && k0 + kNK - 1 <= fmin_hi;
-        const int lo_eff = full ? -0x7fffffff : my_lo - k0;
-        const int hi_eff = full ? 0x7fffffff : my_hi - k0;
+        const bool full = fmax_lo <= k0 && k0 + kNK - 1 <= fmin_hi;   // same for the workgroup
         float sv[16];
-        float mx = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int kk = 8 * (e >> 2) + 4 * half + (e & 3);
-          const bool ok = kk >= lo_eff && kk <= hi_eff;
-          sv[e] = ok ? sacc[e] * scale_log2 : -INFINITY;
-          mx = fmaxf(mx, sv[e]);
+        for (int e = 0; e < 16; ++e) sv[e] = sacc[e] * scale_log2;
+        if (!full) {
+          const int lo_eff = my_lo - k0, hi_eff = my_hi - k0;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int kk = 8 * (e >> 2) + 4 * half + (e & 3);
+            if (kk < lo_eff || kk > hi_eff) sv[e] = -INFINITY;
+          }
         }
+        float mx = sv[0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sv[e]);
         {
           auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                       false, false);
@@ -273,7 +285,8 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
         for (int e = 0; e < 16; ++e) {
           // a masked score is -inf and gives 0; a row without any valid key so far has
           // m_used = -inf and only masked scores, which must also give 0 (not exp2(NaN))
-          const float p = sv[e] == -INFINITY ? 0.0f : exp2f(sv[e] - m_used);
+          // exp2 arguments lie in [-inf, 64]: the raw v_exp_f32 (no denormal scaling) suffices
+          const float p = sv[e] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sv[e] - m_used);
           const bf16 pb = (bf16)p;
           psum += p;
           wsum += (float)pb;
@@ -290,12 +303,11 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
             const bool lo_part = dt < 4;
             const char* base = lo_part ? vlo : kqk;
             const int stride = lo_part ? 256 : 1024;
-            const int off = ((dt & 1) ? (lo_part ? v_lo_odd : v_hi_odd)
-                                      : (lo_part ? v_lo_even : v_hi_even)) + 64 * dt;
+            const int off = rho_l * stride + v_dt[dt & 3] + 256 * (dt >> 2);
             const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (lds_bf16x4*)(base + off + (16 * ks) * stride));
+                (lds_bf16x4*)(base + off + v_e[0] + (16 * ks) * stride));
             const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (lds_bf16x4*)(base + off + (16 * ks + 8) * stride));
+                (lds_bf16x4*)(base + off + v_e[1] + (16 * ks + 8) * stride));
             bf16x8 vv;
             vv[0] = v0[0]; vv[1] = v0[1]; vv[2] = v0[2]; vv[3] = v0[3];
             vv[4] = v1[0]; vv[5] = v1[1]; vv[6] = v1[2]; vv[7] = v1[3];
