@@ -44,7 +44,7 @@ constexpr int kVloBytes = kNK * kRot * 2;        // 8 KiB
 constexpr int kStageBytes = kKqkBytes + kVloBytes;
 constexpr float kTau = 64.0f;                    // reference-move threshold (log2 units)
 
-typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 // 16-byte chunk swizzle of a tile row (gfx950 LDS conflicts within 256-byte windows): rows
@@ -52,13 +52,27 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 // and rows 4k..4k+3 map a chunk pair to distinct 32-byte slots (the 32-lane transpose reads).
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
-__device__ __forceinline__ void dma16(const void* src, char* lds_row_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_row_base, 16, 0, 0);
+// 16-byte global->LDS load: lane l's bytes land at LDS address lds_row_addr + 16 l.  Issued as inline asm
+// on purpose: the compiler's wait-count model charges these loads to the LDS counter as well, so
+// every LDS-read wait inside the tile loop would also wait for the next tile's loads to arrive
+// from memory.  The kernel orders them itself (s_waitcnt vmcnt + barrier before a stage is read),
+// and no other instruction of the kernel uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_row_addr) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_row_addr);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
+               : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
-// scheduling-group masks of __builtin_amdgcn_sched_group_barrier
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left open) through the builtin, so that the compiler's
+// own wait placement knows that every earlier global load has completed
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// LDS fragments in flight ahead of the MFMA that consumes them (S^T and O^T products)
+constexpr int kDepthK = 4;
+constexpr int kDepthV = 3;
 
 template <bool ROT16>
 __device__ __forceinline__ f32x16 mfma_rot(const bf16x8& a, const bf16x8& b, const f32x16& c) {
@@ -175,9 +189,12 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
       const int64_t krow_bytes = (int64_t)kv_stride * kD * 2, rrow_bytes = (int64_t)kv_stride * a.k_rot_hs * 2;
       const bool rot_lane = l < 16;
       const int lane_row_bytes = (int)(rot_lane ? rrow_bytes : krow_bytes);
+      // LDS destinations as 32-bit addresses, wave-uniform (scalar registers)
+      const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_char*)smem;
+      const int wu = __builtin_amdgcn_readfirstlane(w);
       auto issue = [&](int buf, int k0) {
-        char* kqk = smem + buf * kStageBytes;
-        char* vlo = kqk + kKqkBytes;
+        const uint32_t kqk = smem_lds + buf * kStageBytes;
+        const uint32_t vlo = kqk + kKqkBytes;
         const char* raw_t = (const char*)kraw_b + (int64_t)k0 * krow_bytes;
         const char* lane_t = rot_lane ? krot_b + (int64_t)k0 * rrow_bytes : raw_t;
         const int last = a.n_kv - 1 - k0;
@@ -186,19 +203,19 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
         for (int i = 0; i < 8; ++i) {
           const int row = 8 * w + i;
           const int rr = tail ? min(row, last) : row;
-          dma16(lane_t + (uint32_t)(rr * lane_row_bytes + 16 * (l ^ swz(row))), kqk + row * 1024);
+          dma16(lane_t + (uint32_t)(rr * lane_row_bytes + 16 * (l ^ swz(row))), kqk + (8 * wu + i) * 1024);
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int row = 8 * w + 4 * i + (l >> 4);
           const int rr = tail ? min(row, last) : row;
           dma16(raw_t + (uint32_t)(rr * (int)krow_bytes + 16 * ((l & 15) ^ swz(row))),
-                vlo + (8 * w + 4 * i) * 256);
+                vlo + (8 * wu + 4 * i) * 256);
         }
       };
 
       issue(0, kt0 * kNK);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      wait_vm0();
       __syncthreads();
 
       for (int kt = kt0; kt <= kt1; ++kt) {
@@ -208,21 +225,24 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
         const char* kqk = smem + cur * kStageBytes;
         const char* vlo = kqk + kKqkBytes;
 
-        // ---- S^T = K Q^T over all 512 dims, LDS reads two steps ahead of the MFMAs --------
+        // ---- S^T = K Q^T over all 512 dims --------------------------------------------------
+        // software pipelined: the fragment of step s+kDepthK is requested right after the MFMA of
+        // step s, and scheduling fences keep that order (one wave per SIMD: the LDS latency is
+        // hidden only by the reads in flight)
         f32x16 sacc = f32x16{};
         {
-          bf16x8 kf[32];
-          kf[0] = *(const bf16x8*)(kqk + qk_off[0]);
-          kf[1] = *(const bf16x8*)(kqk + qk_off[1]);
+          bf16x8 kf[kDepthK];
+          auto kld = [&](int s) { return *(const bf16x8*)(kqk + qk_off[s & 7] + 256 * (s >> 3)); };
+#pragma unroll
+          for (int j = 0; j < kDepthK; ++j) kf[j] = kld(j);
 #pragma unroll
           for (int s = 0; s < 32; ++s) {
-            if (s + 2 < 32) kf[s + 2] = *(const bf16x8*)(kqk + qk_off[(s + 2) & 7] + 256 * ((s + 2) >> 3));
             if (s < 8)
-              sacc = mfma_rot<ROT16>(kf[s], q[s], sacc);
+              sacc = mfma_rot<ROT16>(kf[s % kDepthK], q[s], sacc);
             else
-              sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], q[s], sacc, 0, 0, 0);
-            if (s + 2 < 32) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+              sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s % kDepthK], q[s], sacc, 0, 0, 0);
+            if (s + kDepthK < 32) kf[s % kDepthK] = kld(s + kDepthK);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
         // ---- mask, row max, lazy rescale, probabilities --------------------------------------
@@ -295,9 +315,8 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
         l_part += psum;
         w_part += wsum;
 
-        // ---- O^T += V^T P^T, transpose reads two steps ahead of the MFMAs --------------------
+        // ---- O^T += V^T P^T, software pipelined like S^T -------------------------------------
         {
-          bf16x8 vf[32];
           auto vload = [&](int i) {
             const int ks = i >> 4, dt = i & 15;
             const bool lo_part = dt < 4;
@@ -313,17 +332,17 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
             vv[4] = v1[0]; vv[5] = v1[1]; vv[6] = v1[2]; vv[7] = v1[3];
             return vv;
           };
-          vf[0] = vload(0);
-          vf[1] = vload(1);
+          bf16x8 vf[kDepthV];
+#pragma unroll
+          for (int j = 0; j < kDepthV; ++j) vf[j] = vload(j);
 #pragma unroll
           for (int i = 0; i < 32; ++i) {
-            if (i + 2 < 32) vf[i + 2] = vload(i + 2);
-            o[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pk[i >> 4], o[i & 15], 0, 0, 0);
-            if (i + 2 < 32) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            o[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % kDepthV], pk[i >> 4], o[i & 15], 0, 0, 0);
+            if (i + kDepthV < 32) vf[i % kDepthV] = vload(i + kDepthV);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        wait_vm0();
         __syncthreads();
       }
     }
