@@ -66,6 +66,14 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_row_addr) {
 }
 #pragma clang diagnostic pop
 
+// a wave-uniform pointer, placed in scalar registers
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(((uint64_t)hi << 32) | lo);
+}
+
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left open) through the builtin, so that the compiler's
 // own wait placement knows that every earlier global load has completed
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -73,6 +81,8 @@ __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70);
 // LDS fragments in flight ahead of the MFMA that consumes them (S^T and O^T products)
 constexpr int kDepthK = 4;
 constexpr int kDepthV = 3;
+// direct-to-LDS loads per wave and tile
+constexpr int kDmaParts = 10;
 
 template <bool ROT16>
 __device__ __forceinline__ f32x16 mfma_rot(const bf16x8& a, const bf16x8& b, const f32x16& c) {
@@ -192,26 +202,32 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
       // LDS destinations as 32-bit addresses, wave-uniform (scalar registers)
       const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_char*)smem;
       const int wu = __builtin_amdgcn_readfirstlane(w);
-      auto issue = [&](int buf, int k0) {
+      // part j (0..9) of the loads of tile k0..k0+31 into stage buf: parts 0..7 fill kqk row
+      // 8w+j, parts 8..9 fill four vlo rows each
+      auto issue_part = [&](int buf, int k0, int j) {
         const uint32_t kqk = smem_lds + buf * kStageBytes;
         const uint32_t vlo = kqk + kKqkBytes;
-        const char* raw_t = (const char*)kraw_b + (int64_t)k0 * krow_bytes;
-        const char* lane_t = rot_lane ? krot_b + (int64_t)k0 * rrow_bytes : raw_t;
+        // tile bases are wave-uniform: scalar registers, selected per lane
+        const char* raw_t = uniform_ptr((const char*)kraw_b + (int64_t)k0 * krow_bytes);
+        const char* rot_t = uniform_ptr(krot_b + (int64_t)k0 * rrow_bytes);
         const int last = a.n_kv - 1 - k0;
         const bool tail = last < kNK - 1;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int row = 8 * w + i;
+        if (j < 8) {
+          const int row = 8 * w + j;
           const int rr = tail ? min(row, last) : row;
-          dma16(lane_t + (uint32_t)(rr * lane_row_bytes + 16 * (l ^ swz(row))), kqk + (8 * wu + i) * 1024);
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
+          const char* lane_t = rot_lane ? rot_t : raw_t;
+          dma16(lane_t + (uint32_t)(rr * lane_row_bytes + 16 * (l ^ swz(row))), kqk + (8 * wu + j) * 1024);
+        } else {
+          const int i = j - 8;
           const int row = 8 * w + 4 * i + (l >> 4);
           const int rr = tail ? min(row, last) : row;
           dma16(raw_t + (uint32_t)(rr * (int)krow_bytes + 16 * ((l & 15) ^ swz(row))),
                 vlo + (8 * wu + 4 * i) * 256);
         }
+      };
+      auto issue = [&](int buf, int k0) {
+#pragma unroll
+        for (int j = 0; j < kDmaParts; ++j) issue_part(buf, k0, j);
       };
 
       issue(0, kt0 * kNK);
@@ -221,6 +237,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
       for (int kt = kt0; kt <= kt1; ++kt) {
         const int cur = (kt - kt0) & 1;
         const int k0 = kt * kNK;
+        // the next tile's loads, into the other stage (free since the last barrier)
         if (kt < kt1) issue(cur ^ 1, k0 + kNK);
         const char* kqk = smem + cur * kStageBytes;
         const char* vlo = kqk + kKqkBytes;
@@ -246,10 +263,12 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
           }
         }
         // ---- mask, row max, lazy rescale, probabilities --------------------------------------
+        // raw scores: the scale (log2 domain) is applied once to the row max and fused into the
+        // exponent's FMA
         const bool full = fmax_lo <= k0 && k0 + kNK - 1 <= fmin_hi;   // same for the workgroup
         float sv[16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sv[e] = sacc[e] * scale_log2;
+        for (int e = 0; e < 16; ++e) sv[e] = sacc[e];
         if (!full) {
           const int lo_eff = my_lo - k0, hi_eff = my_hi - k0;
 #pragma unroll
@@ -258,13 +277,14 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
             if (kk < lo_eff || kk > hi_eff) sv[e] = -INFINITY;
           }
         }
-        float mx = sv[0];
+        float mx = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
 #pragma unroll
-        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sv[e]);
+        for (int e = 3; e < 15; e += 2) mx = fmaxf(fmaxf(mx, sv[e]), sv[e + 1]);
+        mx = fmaxf(mx, sv[15]);
         {
           auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                       false, false);
-          mx = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1]));
+          mx = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1])) * scale_log2;
         }
         // first valid key of a row: take its tile maximum as the reference (O is still 0)
         if (m_used == -INFINITY) m_used = mx;
@@ -292,6 +312,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
               }
             }
             flushed = true;
+            wait_vm0();   // the output rows are re-read by a later flush
           }
 #pragma unroll
           for (int dt = 0; dt < 16; ++dt) o[dt] = f32x16{};
@@ -299,18 +320,23 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
           w_part *= alpha;
           m_used = m_new;
         }
+        // p = exp2(s * scale_log2 - m_used): a masked score (-inf) gives 0; a row without any
+        // valid key so far has m_used = -inf and only masked scores, so any finite reference
+        // gives the same zeros.  The exponents are <= kTau, so the raw v_exp_f32 suffices.
+        const float neg_m = m_used == -INFINITY ? 0.0f : -m_used;
         bf16x8 pk[2];
         float psum = 0.0f, wsum = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          // a masked score is -inf and gives 0; a row without any valid key so far has
-          // m_used = -inf and only masked scores, which must also give 0 (not exp2(NaN))
-          // exp2 arguments lie in [-inf, 64]: the raw v_exp_f32 (no denormal scaling) suffices
-          const float p = sv[e] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sv[e] - m_used);
-          const bf16 pb = (bf16)p;
-          psum += p;
-          wsum += (float)pb;
-          pk[e >> 3][e & 7] = pb;
+        for (int e = 0; e < 16; e += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], scale_log2, neg_m));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e + 1], scale_log2, neg_m));
+          const bf16x2 pb = {(bf16)p0, (bf16)p1};
+          psum += p0;
+          psum += p1;
+          // sum of the bf16-rounded weights the PV product uses (exact products by one)
+          wsum = __builtin_amdgcn_fdot2_f32_bf16(pb, bf16x2{(bf16)1.0f, (bf16)1.0f}, wsum, false);
+          pk[e >> 3][e & 7] = pb[0];
+          pk[e >> 3][(e & 7) + 1] = pb[1];
         }
         l_part += psum;
         w_part += wsum;
