@@ -16,6 +16,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
 INTRA, SUCC, INTER = 0, 1, 2
+# remap modes: the reading fixed in dca_oracle.c, then the page-literal tables (inter query at c,
+# inter query at 2c; succ = the whole previous chunk in both)
+REMAP_BASELINE, REMAP_PAGE_C, REMAP_PAGE_2C = 0, 1, 2
 
 
 def _lib():
@@ -27,13 +30,13 @@ def _lib():
         lib = ctypes.CDLL(path)
         i64, i32p, f64p = ctypes.c_int64, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)
         lib.dca_oracle_regime.restype = ctypes.c_int
-        lib.dca_oracle_regime.argtypes = [i64, i64, i64, i64]
+        lib.dca_oracle_regime.argtypes = [i64, i64, i64, i64, ctypes.c_int]
         lib.dca_oracle_query_pos.restype = i64
-        lib.dca_oracle_query_pos.argtypes = [i64, i64, ctypes.c_int]
+        lib.dca_oracle_query_pos.argtypes = [i64, i64, ctypes.c_int, ctypes.c_int]
         lib.dca_oracle_key_pos.restype = i64
         lib.dca_oracle_key_pos.argtypes = [i64, i64]
         lib.dca_oracle_remap.restype = i64
-        lib.dca_oracle_remap.argtypes = [i64, i64, i32p, i64, i32p, i32p, i32p, ctypes.c_int]
+        lib.dca_oracle_remap.argtypes = [i64, ctypes.c_int, i64, i32p, i64, i32p, i32p, i32p, ctypes.c_int]
         lib.dca_oracle_rope.restype = None
         lib.dca_oracle_rope.argtypes = [i64, i64, ctypes.c_double, f64p, f64p,
                                         ctypes.POINTER(ctypes.c_int64), i64, i64, f64p]
@@ -41,7 +44,7 @@ def _lib():
         lib.dca_oracle_merge.argtypes = [i64, f64p, f64p, i64, i64, f64p, f64p]
         lib.dca_oracle_attention.restype = ctypes.c_int
         lib.dca_oracle_attention.argtypes = [
-            i64, i64, i64, i64, i64, ctypes.c_double, ctypes.c_double, f64p, ctypes.c_int,
+            i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_double, ctypes.c_double, f64p, ctypes.c_int,
             ctypes.c_int, i64, i64, ctypes.c_void_p, i32p, ctypes.c_void_p, i64, i64,
             ctypes.POINTER(ctypes.c_int64), f64p, f64p, f64p, f64p, ctypes.c_int]
         _LIB = lib
@@ -52,15 +55,16 @@ def _ptr(a, ctype):
     return a.ctypes.data_as(ctypes.POINTER(ctype))
 
 
-def regime(i, j, c, n_kv):
+def regime(i, j, c, n_kv, mode=REMAP_BASELINE):
     """Regime of key j for a query at i (DCA feature page, "Section C design" table, read as in
-    the header of dca_oracle.c); -1 when the key is not attended."""
-    return _lib().dca_oracle_regime(int(i), int(j), int(c), int(n_kv))
+    the header of dca_oracle.c, or literally for the page modes); -1 when the key is not attended."""
+    return _lib().dca_oracle_regime(int(i), int(j), int(c), int(n_kv), int(mode))
 
 
-def query_pos(i, c, r):
-    """Remapped query position of regime r (intra i mod c, succ (i mod c)+c, inter c-1)."""
-    return _lib().dca_oracle_query_pos(int(i), int(c), int(r))
+def query_pos(i, c, r, mode=REMAP_BASELINE):
+    """Remapped query position of regime r (intra i mod c, succ (i mod c)+c, inter c-1; the page
+    modes put inter at c or 2c)."""
+    return _lib().dca_oracle_query_pos(int(i), int(c), int(r), int(mode))
 
 
 def key_pos(j, c):
@@ -68,7 +72,7 @@ def key_pos(j, c):
     return _lib().dca_oracle_key_pos(int(j), int(c))
 
 
-def remap(c, qpos, n_kv, n_threads=0):
+def remap(c, qpos, n_kv, n_threads=0, mode=REMAP_BASELINE):
     """Positions and per-regime key intervals by enumeration of the explicit predicate.
 
     Returns (pos_q int32 [3, rows], pos_k int32 [n_kv], bounds int32 [3, rows, 2], status);
@@ -78,7 +82,7 @@ def remap(c, qpos, n_kv, n_threads=0):
     pos_q = np.zeros((3, rows), np.int32)
     pos_k = np.zeros((max(n_kv, 0),), np.int32)
     bounds = np.zeros((3, rows, 2), np.int32)
-    st = _lib().dca_oracle_remap(int(c), rows, _ptr(qpos, ctypes.c_int32), int(n_kv),
+    st = _lib().dca_oracle_remap(int(c), int(mode), rows, _ptr(qpos, ctypes.c_int32), int(n_kv),
                                  _ptr(pos_q, ctypes.c_int32), _ptr(pos_k, ctypes.c_int32),
                                  _ptr(bounds, ctypes.c_int32), int(n_threads))
     return pos_q, pos_k, bounds, int(st)
@@ -113,13 +117,14 @@ def merge(o_parts, lse_parts):
 
 
 def attention(q, qpos, k, *, chunk, n_rot, theta, scale, freq_factors=None, rows=None,
-              per_regime=True, n_threads=0, round_rotated_bf16=False):
+              per_regime=True, n_threads=0, round_rotated_bf16=False, remap_mode=REMAP_BASELINE):
     """DCA attention of selected query rows in fp64.
 
     q [B, T, Hq, D] and k [B, N, Hkv, D] are float32 arrays or uint16 bf16 bit patterns (same
     kind for both); qpos int32 [B, T]; rows = flat row indices b*T+t (default: all).
     round_rotated_bf16: round the rotated dims of queries and keys to bf16 before the scores
     (the contract of a caller passing bf16 rotated operands to the per-regime entry point).
+    remap_mode: REMAP_BASELINE (the reading of dca_oracle.c) or a page-literal mode.
     Returns dict(o [n, Hq, D], lse [n, Hq], o_reg [3, n, Hq, D], lse_reg [3, n, Hq], rows)."""
     q = np.ascontiguousarray(q)
     k = np.ascontiguousarray(k)
@@ -141,7 +146,7 @@ def attention(q, qpos, k, *, chunk, n_rot, theta, scale, freq_factors=None, rows
     lse_reg = np.zeros((3, n, Hq), np.float64) if per_regime else None
     ff = None if freq_factors is None else np.ascontiguousarray(freq_factors, dtype=np.float64)
     st = _lib().dca_oracle_attention(
-        D, int(n_rot), Hq, Hkv, int(chunk), float(theta), float(scale),
+        D, int(n_rot), Hq, Hkv, int(chunk), int(remap_mode), float(theta), float(scale),
         None if ff is None else _ptr(ff, ctypes.c_double), in_bf16, 1 if round_rotated_bf16 else 0, B, T,
         q.ctypes.data_as(ctypes.c_void_p), _ptr(qpos, ctypes.c_int32),
         k.ctypes.data_as(ctypes.c_void_p), N, n, _ptr(sel, ctypes.c_int64),

@@ -34,6 +34,14 @@
  *   with intra, so intra and succ see the true distance i - j) and moves previous-chunk keys at
  *   distance >= c into inter.
  *
+ * Page-literal remap modes (mode argument; 0 is the reading above):
+ *   mode 1: the [F] "Section C design" table as printed: succ holds the whole previous chunk
+ *           (chunk(j) == chunk(i) - 1), inter every older chunk (chunk(j) < chunk(i) - 1), and
+ *           the inter query sits at c.  Distances: intra and succ i - j (succ up to 2c - 1),
+ *           inter c - (j mod c) in [1, c].
+ *   mode 2: as mode 1 with the inter query at 2c ([U] entry "opencoti F5 dca", its fused kernel
+ *           and the #635 cache fill).  Inter distances 2c - (j mod c) in [c + 1, 2c].
+ *
  * RoPE reading: rotary dims [0, n_rot) form pairs (f, f + n_rot/2); for pair f,
  *   a = p * theta^(-2f/n_rot) / ff[f];
  *   y_f = x_f cos a - x_{f+n_rot/2} sin a;  y_{f+n_rot/2} = x_f sin a + x_{f+n_rot/2} cos a.
@@ -65,19 +73,22 @@ static int64_t pos_mod(int64_t a, int64_t b) { return a - floor_div(a, b) * b; }
 
 /* Regime of key j for a query at position i ([F] "Section C design" table, with the reading
  * above).  Returns -1 when the key is not attended (j > i, j < 0 or j >= n_kv). */
-int dca_oracle_regime(int64_t i, int64_t j, int64_t c, int64_t n_kv) {
+int dca_oracle_regime(int64_t i, int64_t j, int64_t c, int64_t n_kv, int mode) {
   if (j < 0 || j > i || j >= n_kv) return -1;
   int64_t ci = floor_div(i, c), cj = floor_div(j, c);
   if (cj == ci) return OR_INTRA;
+  if (mode != 0) return cj == ci - 1 ? OR_SUCC : OR_INTER; /* page table: by chunk alone */
   if (cj == ci - 1 && i - j < c) return OR_SUCC;
   if (i - j >= c) return OR_INTER;
   return -2; /* unreachable: a key in an older chunk is always at distance >= c */
 }
 
 /* Remapped query position of regime r for a query at i. */
-int64_t dca_oracle_query_pos(int64_t i, int64_t c, int r) {
+int64_t dca_oracle_query_pos(int64_t i, int64_t c, int r, int mode) {
   if (r == OR_INTRA) return pos_mod(i, c);
   if (r == OR_SUCC) return pos_mod(i, c) + c;
+  if (mode == 1) return c;
+  if (mode == 2) return 2 * c;
   return c - 1;
 }
 
@@ -89,7 +100,7 @@ int64_t dca_oracle_key_pos(int64_t j, int64_t c) { return pos_mod(j, c); }
  * [3][n_rows][2] (inclusive lo, hi; empty = (0, -1)).  Any output may be NULL.
  * Returns 0, or -(row+1) for the first row whose regime key set is not one contiguous
  * interval, or -(n_rows+1) if the predicate reached its unreachable branch. */
-int64_t dca_oracle_remap(int64_t c, int64_t n_rows, const int32_t* qpos, int64_t n_kv,
+int64_t dca_oracle_remap(int64_t c, int mode, int64_t n_rows, const int32_t* qpos, int64_t n_kv,
                          int32_t* pos_q, int32_t* pos_k, int32_t* bounds, int n_threads) {
   int64_t status = 0;
 #ifdef _OPENMP
@@ -103,13 +114,13 @@ int64_t dca_oracle_remap(int64_t c, int64_t n_rows, const int32_t* qpos, int64_t
   for (int64_t row = 0; row < n_rows; ++row) {
     int64_t i = qpos[row];
     for (int r = 0; r < 3; ++r) {
-      if (pos_q) pos_q[r * n_rows + row] = (int32_t)dca_oracle_query_pos(i, c, r);
+      if (pos_q) pos_q[r * n_rows + row] = (int32_t)dca_oracle_query_pos(i, c, r, mode);
     }
     int64_t lo[3] = {-1, -1, -1}, hi[3] = {-1, -1, -1}, cnt[3] = {0, 0, 0};
     int bad = 0;
     int64_t jmax = i < n_kv - 1 ? i : n_kv - 1;
     for (int64_t j = 0; j <= jmax; ++j) {
-      int r = dca_oracle_regime(i, j, c, n_kv);
+      int r = dca_oracle_regime(i, j, c, n_kv, mode);
       if (r < 0) { bad = 2; continue; }
       if (cnt[r] == 0) lo[r] = j;
       hi[r] = j;
@@ -212,14 +223,14 @@ void dca_oracle_merge(int64_t n_parts, const double* o_parts, const double* lse_
  * the scores are formed: the contract of a caller that hands over bf16 rotated operands (used to
  * check the per-regime entry point); 0 keeps them exact.
  * Returns 0, or -1 on allocation failure, -2 on a bad argument. */
-int dca_oracle_attention(int64_t D, int64_t n_rot, int64_t Hq, int64_t Hkv, int64_t c,
+int dca_oracle_attention(int64_t D, int64_t n_rot, int64_t Hq, int64_t Hkv, int64_t c, int mode,
                          double theta, double scale, const double* ff, int in_bf16, int rot_round,
                          int64_t B,
                          int64_t T, const void* q, const int32_t* qpos, const void* k, int64_t n_kv,
                          int64_t n_sel, const int64_t* sel, double* o, double* lse, double* o_reg,
                          double* lse_reg, int n_threads) {
   if (D <= 0 || n_rot <= 0 || n_rot > D || n_rot > 1024 || (n_rot & 1) || Hq <= 0 || Hkv <= 0 ||
-      Hq % Hkv || c <= 0 || B <= 0 || T <= 0 || n_kv < 0)
+      Hq % Hkv || c <= 0 || mode < 0 || mode > 2 || B <= 0 || T <= 0 || n_kv < 0)
     return -2;
 #ifdef _OPENMP
   if (n_threads > 0) omp_set_num_threads(n_threads);
@@ -270,14 +281,14 @@ int dca_oracle_attention(int64_t D, int64_t n_rot, int64_t Hq, int64_t Hkv, int6
           int64_t g = h / G;
           for (int64_t d = 0; d < D; ++d) qv[d] = load_in(q, (flat * Hq + h) * D + d, in_bf16);
           for (int r = 0; r < 3; ++r) {
-            rope_one(n_rot, D, theta, ff, qv, (double)dca_oracle_query_pos(i, c, r), qr + r * D);
+            rope_one(n_rot, D, theta, ff, qv, (double)dca_oracle_query_pos(i, c, r, mode), qr + r * D);
             if (rot_round == 1)
               for (int64_t d = 0; d < n_rot; ++d) qr[r * D + d] = round_bf16(qr[r * D + d]);
           }
           int64_t jmax = i < n_kv - 1 ? i : n_kv - 1;
           /* scores of every attended key, each with its own regime's query rotation */
           for (int64_t j = 0; j <= jmax; ++j) {
-            int r = dca_oracle_regime(i, j, c, n_kv);
+            int r = dca_oracle_regime(i, j, c, n_kv, mode);
             r_buf[j] = (signed char)r;
             const double* qq = qr + (r < 0 ? 0 : r) * D;
             double dot = 0.0;

@@ -47,6 +47,61 @@ def test_remap_golden_table(case):
     assert pos_k.tolist() == [j % 4 for j in range(n_kv)]
 
 
+def _load_golden_remap_page():
+    rows = []
+    with open(os.path.join(GOLDEN, "remap_c4_page.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            a, b, c = line.split("|")
+            mode, i, n_kv = map(int, a.split())
+            rows.append((mode, i, n_kv, list(map(int, b.split())), list(map(int, c.split()))))
+    return rows
+
+
+@pytest.mark.parametrize("case", _load_golden_remap_page(), ids=lambda c: f"m{c[0]}_i{c[1]}_n{c[2]}")
+def test_remap_golden_table_page_modes(case):
+    mode, i, n_kv, pq, bd = case
+    pos_q, pos_k, bounds, st = oracle.remap(4, [i], n_kv, mode=mode)
+    assert st == 0
+    assert pos_q[:, 0].tolist() == pq
+    assert bounds[:, 0, :].reshape(-1).tolist() == bd
+    assert pos_k.tolist() == [j % 4 for j in range(n_kv)]
+
+
+@pytest.mark.parametrize("mode", [oracle.REMAP_PAGE_C, oracle.REMAP_PAGE_2C])
+@pytest.mark.parametrize("c", [1, 2, 3, 4, 7, 16])
+def test_remap_page_modes_partition_and_distances(c, mode):
+    """Page-literal tables ("Section C design"): regimes by chunk index alone, still a partition
+    of the causal keys; intra and succ see the true distance (succ up to 2c - 1), inter sees
+    P_inter - (j mod c) with P_inter = c (distances [1, c]) or 2c (distances [c + 1, 2c])."""
+    n_kv = 90
+    qpos = np.arange(0, n_kv + 6, dtype=np.int32)
+    pos_q, pos_k, bounds, st = oracle.remap(c, qpos, n_kv, mode=mode)
+    assert st == 0
+    p_inter = c if mode == oracle.REMAP_PAGE_C else 2 * c
+    for row, i in enumerate(qpos):
+        seen = np.zeros(n_kv, np.int32)
+        for r in range(3):
+            lo, hi = bounds[r, row]
+            if hi < lo:
+                assert (lo, hi) == (0, -1)
+                continue
+            seen[lo:hi + 1] += 1
+            for j in range(lo, hi + 1):
+                assert oracle.regime(i, j, c, n_kv, mode) == r
+                chunk_gap = i // c - j // c
+                assert chunk_gap == r if r != oracle.INTER else chunk_gap >= 2
+                d = int(pos_q[r, row]) - int(pos_k[j])
+                if r == oracle.INTER:
+                    assert pos_q[r, row] == p_inter and d == p_inter - j % c
+                else:
+                    assert d == i - j and 0 <= d < 2 * c
+        upto = min(int(i), n_kv - 1)
+        assert (seen[: upto + 1] == 1).all() and (seen[upto + 1:] == 0).all()
+
+
 @pytest.mark.parametrize("c", [1, 2, 3, 4, 7, 16, 64])
 def test_remap_partition_and_distances(c):
     """The three regimes partition the causal keys (DCA feature page, "Section C design") and
@@ -325,10 +380,12 @@ def test_attention_single_key_row():
 
 
 @pytest.mark.parametrize("i,c,n_kv", [(37, 8, 38), (63, 16, 64), (40, 16, 41), (100, 7, 101)])
-def test_attention_distance_probe(i, c, n_kv):
+@pytest.mark.parametrize("mode", [oracle.REMAP_BASELINE, oracle.REMAP_PAGE_C, oracle.REMAP_PAGE_2C])
+def test_attention_distance_probe(i, c, n_kv, mode):
     """Probe: q's rotary part is (1,0) in pair 0 and zero elsewhere, k's rotary part is (0,1) in
     pair 0, tails of q are zero.  Then s_j = scale * A * sin(d_j w_0) with d_j the remapped
-    distance: i - j for intra and succ, c - 1 - (j mod c) for inter.  O's rotary dims equal the
+    distance: i - j for intra and succ, c - 1 - (j mod c) for inter (page modes: succ is the whole
+    previous chunk, inter at c - (j mod c) or 2c - (j mod c)).  O's rotary dims equal the
     un-rotated key value (0, 1) exactly because values are not rotated."""
     D, n_rot, half, A, scale = 16, 8, 4, 3.0, 0.5
     ff = np.array([1.7, 2.0, 3.0, 5.0])
@@ -339,11 +396,16 @@ def test_attention_distance_probe(i, c, n_kv):
     k[0, :, 0, half] = 1.0
     k[0, :, 0, n_rot:] = rng.standard_normal((n_kv, D - n_rot)).astype(np.float32)
     res = oracle.attention(q, np.array([[i]], np.int32), k, chunk=c, n_rot=n_rot, theta=1e6,
-                           scale=scale, freq_factors=ff)
+                           scale=scale, freq_factors=ff, remap_mode=mode)
     j = np.arange(min(i, n_kv - 1) + 1)
     same = (j // c) == (i // c)
-    near = (i - j) < c
-    d = np.where(same | near, i - j, c - 1 - (j % c))
+    if mode == oracle.REMAP_BASELINE:
+        near = (i - j) < c
+        d = np.where(same | near, i - j, c - 1 - (j % c))
+    else:
+        near = (j // c) == (i // c) - 1
+        p_inter = c if mode == oracle.REMAP_PAGE_C else 2 * c
+        d = np.where(same | near, i - j, p_inter - (j % c))
     s = scale * A * np.sin(d / ff[0])
     p = scipy.special.softmax(s)
     assert res["lse"][0, 0] == pytest.approx(scipy.special.logsumexp(s), rel=1e-13)
