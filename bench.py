@@ -106,24 +106,77 @@ def time_leg(torch, dca, w, inp, steps, warmup):
     return total_ms / steps, stages.mean(axis=0)
 
 
-def cpu_baseline(w, inp, n_rows, seed=0):
-    import oracle
-    rng = np.random.default_rng(seed)
-    T = w.T
-    # rows spread uniformly over the sequence, so the mean key count matches the workload's
-    ts = np.unique(((np.arange(n_rows) + rng.random(n_rows)) * T / n_rows).astype(np.int64))
-    rows = ts  # B = 1 for prefill workloads; for decode rows are (b, 0)
+def sample_rows(w, n_rows, seed=0):
+    """Query rows for the oracle timing: every chunk at local offsets {0, 1, c/2, c-2, c-1}, then
+    uniformly drawn rows up to n_rows (prefill); all B rows (decode)."""
     if w.T == 1:
-        rows = np.arange(min(w.B, n_rows), dtype=np.int64)
+        return np.arange(w.B, dtype=np.int64)
+    rng = np.random.default_rng(seed)
+    pos = w.q0 + np.arange(w.T, dtype=np.int64)
+    picked = set()
+    for c0 in range(int(pos[0] // w.chunk) * w.chunk, int(pos[-1]) + 1, w.chunk):
+        for off in (0, 1, w.chunk // 2, w.chunk - 2, w.chunk - 1):
+            p = c0 + off
+            if pos[0] <= p <= pos[-1]:
+                picked.add(int(p - w.q0))
+    rest = np.setdiff1d(np.arange(w.T), np.fromiter(picked, dtype=np.int64, count=len(picked)))
+    extra = max(0, n_rows - len(picked))
+    if extra:
+        picked.update(int(t) for t in rng.choice(rest, size=min(extra, rest.size), replace=False))
+    return np.array(sorted(picked), dtype=np.int64)
+
+
+def cpu_baseline(w, inp, n_rows, seed=0):
+    """The fp64 CPU oracle, timed on a sample of query rows of the same workload (all heads), on
+    every host thread.  Reported as attended (query, key) pairs per second and as the query
+    tokens per second that rate gives on the full workload."""
+    import oracle
+    rows = sample_rows(w, n_rows, seed)
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     ff = inp["freq_factors"].astype(np.float64)
     t0 = time.perf_counter()
     oracle.attention(inp["q"], inp["q_pos"], inp["k"], chunk=w.chunk, n_rot=w.n_rot, theta=w.theta,
                      scale=w.scale, freq_factors=ff, rows=rows, per_regime=False, n_threads=threads)
     dt = time.perf_counter() - t0
-    return dict(value=len(rows) / dt, unit="tokens/s", cores=threads, kind="oracle",
-                sample=f"{len(rows)} of {w.B * w.T} query rows (all {w.Hq} heads), rows spread "
-                       f"uniformly over the sequence; {dt:.1f} s on {threads} threads")
+    qpos = inp["q_pos"].reshape(-1).astype(np.float64)
+    keys = np.minimum(qpos + 1, w.N)
+    pairs_sample = float(keys[rows].sum()) * w.Hq
+    pairs_full_per_token = float(keys.sum()) / keys.size * w.Hq
+    pairs_per_s = pairs_sample / dt
+    return dict(value=pairs_per_s / pairs_full_per_token, unit="tokens/s", cores=threads, kind="oracle",
+                pairs_per_s=pairs_per_s,
+                sample=f"{len(rows)} of {w.B * w.T} query rows x {w.Hq} heads ({pairs_sample:.3g} pairs): "
+                       f"every chunk at local offsets 0, 1, c/2, c-2, c-1 plus uniform rows; {dt:.1f} s "
+                       f"on {threads} threads (fp64 oracle incl. its key rotation); value = measured "
+                       f"pairs/s over the workload's mean pairs per token")
+
+
+def measured_peaks(torch, dca):
+    """On-box reference rates from the library's probe kernels (include/dca_calibrate.h): bf16
+    MFMA 32x32x16 with no memory traffic (2048 workgroups of 4 waves), and a streaming read of
+    4 GiB with 16-byte loads (8192 workgroups)."""
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+    n_wg, iters = 2048, 2000
+    sink = torch.empty((8192 * 256,), dtype=torch.float32, device="cuda:0")
+    t = timed(lambda: dca.probe_mfma_bf16(n_wg, iters, sink), 5)
+    mfma = n_wg * 4 * iters * 32 * 32768.0 / t / 1e12
+    x = torch.empty((1 << 32,), dtype=torch.uint8, device="cuda:0")
+    x.fill_(1)
+    t = timed(lambda: dca.probe_hbm_read(x, 8192, sink), 10)
+    read = x.numel() / t / 1e9
+    del x, sink
+    return {"mfma_bf16_tflops": mfma, "hbm_read_gbps": read,
+            "how": "dca_probe_mfma_bf16 (2048 x 4 waves, 32x32x16 bf16, no memory traffic); "
+                   "dca_probe_hbm_read over 4 GiB"}
 
 
 def main():
@@ -134,9 +187,10 @@ def main():
     ap.add_argument("--workload", default="prefill-32k-c8192")
     ap.add_argument("--decode-workload", default="decode-b8-kv256k-c65536")
     ap.add_argument("--decode-steps", type=int, default=20)
-    ap.add_argument("--cpu-rows", type=int, default=96)
+    ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-measured-peaks", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for the traffic counters)")
     args = ap.parse_args()
@@ -204,9 +258,23 @@ def main():
         torch.cuda.synchronize()
         rec["copy_calibration_bytes"] = int(src.numel() * 4)
         del src, dst
+    if not args.no_measured_peaks:
+        pk = measured_peaks(torch, dca)
+        rec["roofline"]["measured_peak"] = pk["mfma_bf16_tflops"]
+        rec["roofline"]["frac_of_measured_peak"] = rec["roofline"]["achieved"] / pk["mfma_bf16_tflops"]
+        if "decode" in rec:
+            rd = rec["decode"]["roofline"]
+            rd["measured_peak"] = pk["hbm_read_gbps"]
+            rd["frac_of_measured_peak"] = rd["achieved"] / pk["hbm_read_gbps"]
+        rec["measured_peaks"] = pk
     if not args.no_cpu_baseline:
         inp = synth.make_inputs(w)
         rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_rows)
+        del inp
+        if "decode" in rec:
+            inpd = synth.make_inputs(synth.WORKLOADS[args.decode_workload])
+            rec["decode"]["cpu_baseline"] = cpu_baseline(synth.WORKLOADS[args.decode_workload], inpd, args.cpu_rows)
+            del inpd
     print(json.dumps(rec), flush=True)
 
 

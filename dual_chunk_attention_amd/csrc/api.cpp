@@ -8,6 +8,7 @@
 #include <string>
 
 #include "../../include/dca.h"
+#include "../../include/dca_calibrate.h"
 #include "common.h"
 
 namespace {
@@ -55,8 +56,8 @@ dca_status check_config(const dca_config* cfg, int dtype) {
     return fail(DCA_ERR_INVALID_ARGUMENT, "n_head_q %d must be a positive multiple of n_head_kv %d",
                 cfg->n_head_q, cfg->n_head_kv);
   if (cfg->chunk < 1) return fail(DCA_ERR_INVALID_ARGUMENT, "chunk %d < 1", cfg->chunk);
-  if (cfg->remap_mode != 0)
-    return fail(DCA_ERR_UNSUPPORTED, "remap_mode %d not implemented", cfg->remap_mode);
+  if (cfg->remap_mode < DCA_REMAP_BASELINE || cfg->remap_mode > DCA_REMAP_PAGE_2C)
+    return fail(DCA_ERR_INVALID_ARGUMENT, "remap_mode %d is not a dca_remap_mode", cfg->remap_mode);
   if (!(cfg->rope_theta > 0.0f) || !isfinite(cfg->rope_theta))
     return fail(DCA_ERR_INVALID_ARGUMENT, "rope_theta must be finite and > 0");
   if (!isfinite(cfg->scale)) return fail(DCA_ERR_INVALID_ARGUMENT, "scale must be finite");
@@ -180,12 +181,13 @@ dca_status dca_remap_positions(const dca_config* cfg, int32_t B, int32_t T, cons
                                hipStream_t stream) {
   if (!cfg) return fail(DCA_ERR_INVALID_ARGUMENT, "config is NULL");
   if (cfg->chunk < 1) return fail(DCA_ERR_INVALID_ARGUMENT, "chunk %d < 1", cfg->chunk);
-  if (cfg->remap_mode != 0) return fail(DCA_ERR_UNSUPPORTED, "remap_mode %d not implemented", cfg->remap_mode);
+  if (cfg->remap_mode < DCA_REMAP_BASELINE || cfg->remap_mode > DCA_REMAP_PAGE_2C)
+    return fail(DCA_ERR_INVALID_ARGUMENT, "remap_mode %d is not a dca_remap_mode", cfg->remap_mode);
   dca_status st = check_sizes(B, T, n_kv);
   if (st) return st;
   const int64_t rows = (int64_t)B * T;
   if (rows > 0 && !q_pos && (pos_q || bounds)) return fail(DCA_ERR_INVALID_ARGUMENT, "q_pos is NULL");
-  return hip_status(dca::launch_remap(q_pos, rows, cfg->chunk, n_kv, pos_q, pos_k, bounds, stream),
+  return hip_status(dca::launch_remap(q_pos, rows, cfg->chunk, cfg->remap_mode, n_kv, pos_q, pos_k, bounds, stream),
                     "remap launch");
 }
 
@@ -339,7 +341,7 @@ dca_status dca_attention(const dca_config* cfg, dca_dtype dtype, int32_t B, int3
   const int64_t Hq = cfg->n_head_q, R = cfg->n_rot, D = cfg->head_dim;
 
   if ((st = hip_status(mark(0, stream), "stage event"))) return st;
-  if ((st = hip_status(dca::launch_remap(q_pos, rows, cfg->chunk, n_kv, pos_q, nullptr, bounds, stream),
+  if ((st = hip_status(dca::launch_remap(q_pos, rows, cfg->chunk, cfg->remap_mode, n_kv, pos_q, nullptr, bounds, stream),
                        "remap launch")))
     return st;
   if ((st = hip_status(mark(1, stream), "stage event"))) return st;
@@ -445,6 +447,24 @@ dca_status dca_attention(const dca_config* cfg, dca_dtype dtype, int32_t B, int3
   m.lse_out = lse;
   if ((st = hip_status(dca::launch_merge(m, o_dtype == DCA_BF16, stream), "merge launch"))) return st;
   return hip_status(mark(5, stream), "stage event");
+}
+
+dca_status dca_probe_mfma_bf16(int32_t n_workgroups, int32_t iters, float* sink, hipStream_t stream) {
+  if (!sink) return fail(DCA_ERR_INVALID_ARGUMENT, "sink is NULL");
+  if (n_workgroups < 1 || n_workgroups > 65536 || iters < 1 || iters > (1 << 20))
+    return fail(DCA_ERR_INVALID_ARGUMENT, "probe size out of range (%d workgroups, %d iters)",
+                n_workgroups, iters);
+  return hip_status(dca::launch_probe_mfma(n_workgroups, iters, sink, stream), "probe launch");
+}
+
+dca_status dca_probe_hbm_read(const void* src, int64_t bytes, int32_t n_workgroups, float* sink,
+                              hipStream_t stream) {
+  if (!sink || (!src && bytes > 0)) return fail(DCA_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (bytes < 0 || bytes % 16 || ((uintptr_t)src & 15))
+    return fail(DCA_ERR_INVALID_ARGUMENT, "bytes must be a non-negative multiple of 16, src 16-byte aligned");
+  if (n_workgroups < 1 || n_workgroups > 65536)
+    return fail(DCA_ERR_INVALID_ARGUMENT, "n_workgroups %d out of range", n_workgroups);
+  return hip_status(dca::launch_probe_read(src, bytes, n_workgroups, sink, stream), "probe launch");
 }
 
 }  // extern "C"

@@ -49,8 +49,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 // ------------------------------------------------------------------------------------------
 
 // Positions and regime intervals.  pos_q [3][rows], bounds [3][rows][2]; pos_k [n_kv].
-hipError_t launch_remap(const int32_t* q_pos, int64_t rows, int32_t chunk, int32_t n_kv,
-                        int32_t* pos_q, int32_t* pos_k, int32_t* bounds, hipStream_t stream);
+hipError_t launch_remap(const int32_t* q_pos, int64_t rows, int32_t chunk, int32_t mode,
+                        int32_t n_kv, int32_t* pos_q, int32_t* pos_k, int32_t* bounds,
+                        hipStream_t stream);
 
 struct RopeArgs {
   const void* x;
@@ -134,5 +135,10 @@ struct DecodeArgs {
   double theta;
 };
 hipError_t launch_attn_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+
+// reference-rate probes (calibrate.hip)
+hipError_t launch_probe_mfma(int32_t n_workgroups, int32_t iters, float* sink, hipStream_t stream);
+hipError_t launch_probe_read(const void* src, int64_t bytes, int32_t n_workgroups, float* sink,
+                             hipStream_t stream);
 
 }  // namespace dca

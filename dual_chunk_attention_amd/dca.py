@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libdca.so")
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(5)
 F32, BF16 = 0, 1
 INTRA, SUCC, INTER = 0, 1, 2
+REMAP_BASELINE, REMAP_PAGE_C, REMAP_PAGE_2C = 0, 1, 2   # dca_remap_mode
 MAX_MERGE_PARTS = 8
 
 
@@ -62,8 +63,10 @@ def lib():
         L.dca_set_stage_events.argtypes = [vp, i32]
         L.dca_set_stage_events.restype = ctypes.c_int
         L.dca_last_error.restype = ctypes.c_char_p
+        L.dca_probe_mfma_bf16.argtypes = [i32, i32, vp, vp]
+        L.dca_probe_hbm_read.argtypes = [vp, i64, i32, vp, vp]
         for f in ("dca_remap_positions", "dca_rope_partial", "dca_attn_regime", "dca_lse_merge",
-                  "dca_attention"):
+                  "dca_attention", "dca_probe_mfma_bf16", "dca_probe_hbm_read"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -217,3 +220,17 @@ def set_stage_events(events_array) -> None:
         _check(lib().dca_set_stage_events(None, 0))
     else:
         _check(lib().dca_set_stage_events(ctypes.cast(events_array, ctypes.c_void_p), len(events_array)))
+
+
+def probe_mfma_bf16(n_workgroups: int, iters: int, sink: torch.Tensor) -> None:
+    """dca_probe_mfma_bf16 (include/dca_calibrate.h): matrix-core loop on the current stream;
+    sink fp32 [n_workgroups * 256]."""
+    assert sink.dtype == torch.float32 and sink.numel() >= n_workgroups * 256
+    _check(lib().dca_probe_mfma_bf16(n_workgroups, iters, _ptr(sink), _stream()))
+
+
+def probe_hbm_read(src: torch.Tensor, n_workgroups: int, sink: torch.Tensor) -> None:
+    """dca_probe_hbm_read: streaming read of src's bytes on the current stream."""
+    assert src.is_contiguous() and sink.dtype == torch.float32 and sink.numel() >= n_workgroups * 256
+    _check(lib().dca_probe_hbm_read(_ptr(src), src.numel() * src.element_size(), n_workgroups,
+                                    _ptr(sink), _stream()))

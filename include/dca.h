@@ -73,6 +73,22 @@ typedef enum dca_dtype { DCA_F32 = 0, DCA_BF16 = 1 } dca_dtype;
 
 typedef enum dca_regime { DCA_INTRA = 0, DCA_SUCC = 1, DCA_INTER = 2 } dca_regime;
 
+/* Remap rules (dca_config.remap_mode).  Keys always sit at j mod c, the intra regime is the
+ * query's own chunk with the query at i mod c, and the succ query sits at (i mod c) + c.
+ *  DCA_REMAP_BASELINE: the rule stated at the top of this header: succ = previous-chunk keys
+ *      closer than c, inter = every key at distance >= c with the query at c - 1, so every rotary
+ *      distance is below c.
+ *  DCA_REMAP_PAGE_C: the "Section C design" table of the DCA feature page as printed: succ =
+ *      the whole previous chunk (distances up to 2c - 1), inter = every older chunk with the
+ *      query at c.
+ *  DCA_REMAP_PAGE_2C: as DCA_REMAP_PAGE_C with the inter query at 2c (Upstream Sync page, entry
+ *      "opencoti F5 dca": the fused kernel and the dense cache fill). */
+typedef enum dca_remap_mode {
+  DCA_REMAP_BASELINE = 0,
+  DCA_REMAP_PAGE_C = 1,
+  DCA_REMAP_PAGE_2C = 2
+} dca_remap_mode;
+
 #define DCA_N_REGIMES 3
 #define DCA_MAX_MERGE_PARTS 8
 
@@ -83,7 +99,7 @@ typedef struct dca_config {
   int32_t n_head_q;     /* Hq */
   int32_t n_head_kv;    /* Hkv; Hq % Hkv == 0 */
   int32_t chunk;        /* c >= 1 */
-  int32_t remap_mode;   /* 0 only (the rule stated at the top of this header) */
+  int32_t remap_mode;   /* dca_remap_mode; other values: DCA_ERR_INVALID_ARGUMENT */
   float rope_theta;     /* > 0; e.g. 1e6 */
   float scale;          /* score scale, e.g. 1/sqrt(512) */
   const float* freq_factors; /* device fp32 [n_rot/2], each > 0; NULL means all 1.0 */

@@ -24,10 +24,10 @@ def to_dev(arr):
     return torch.from_numpy(np.ascontiguousarray(arr)).to(dev())
 
 
-def cfg_for(w, ff_dev=None, chunk=None):
+def cfg_for(w, ff_dev=None, chunk=None, remap_mode=0):
     return dca.Config(head_dim=w.D, n_rot=w.n_rot, n_head_q=w.Hq, n_head_kv=w.Hkv,
                       chunk=w.chunk if chunk is None else chunk, rope_theta=w.theta, scale=w.scale,
-                      freq_factors=ff_dev)
+                      freq_factors=ff_dev, remap_mode=remap_mode)
 
 
 def assert_o_close(got, want, atol=O_ATOL, what="O"):

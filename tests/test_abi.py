@@ -12,9 +12,14 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def declared_functions():
-    src = open(os.path.join(ROOT, "include", "dca.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(dca_[a-z_]+)\s*\(", src)))
+    """Every dca_* function declared by the headers under include/."""
+    inc = os.path.join(ROOT, "include")
+    names = set()
+    for h in sorted(os.listdir(inc)):
+        if h.endswith(".h"):
+            src = re.sub(r"/\*.*?\*/", "", open(os.path.join(inc, h)).read(), flags=re.S)
+            names.update(re.findall(r"\b(dca_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_header_declares_the_five_operations():
@@ -45,7 +50,8 @@ def _cfg(**kw):
     (dict(n_rot=1024), dca.ERR_INVALID_ARGUMENT),
     (dict(n_head_q=15), dca.ERR_INVALID_ARGUMENT),
     (dict(chunk=0), dca.ERR_INVALID_ARGUMENT),
-    (dict(remap_mode=1), dca.ERR_UNSUPPORTED),
+    (dict(remap_mode=3), dca.ERR_INVALID_ARGUMENT),
+    (dict(remap_mode=-1), dca.ERR_INVALID_ARGUMENT),
     (dict(head_dim=256), dca.ERR_UNSUPPORTED),   # bf16 path is head_dim 512 only
     (dict(n_head_q=64, n_head_kv=1), dca.ERR_UNSUPPORTED),
 ])

@@ -22,11 +22,13 @@ def _inputs(w, **kw):
     return inp, w, ff
 
 
-def _oracle_attention(inp, w, rows=None, chunk=None, per_regime=True, round_rotated_bf16=False):
+def _oracle_attention(inp, w, rows=None, chunk=None, per_regime=True, round_rotated_bf16=False,
+                      remap_mode=0):
     ff = inp["freq_factors"].astype(np.float64) if w.ff_uniform else None
     return oracle.attention(inp["q"], inp["q_pos"], inp["k"], chunk=w.chunk if chunk is None else chunk,
                             n_rot=w.n_rot, theta=w.theta, scale=w.scale, freq_factors=ff, rows=rows,
-                            per_regime=per_regime, round_rotated_bf16=round_rotated_bf16)
+                            per_regime=per_regime, round_rotated_bf16=round_rotated_bf16,
+                            remap_mode=remap_mode)
 
 
 # ----------------------------------------------------------------------------------------------
@@ -54,6 +56,37 @@ def test_remap_bit_exact_edge_positions(c, n_kv):
     pos_q, pos_k, bounds = dca.remap_positions(cfg, to_dev(q_pos), n_kv)
     torch.cuda.synchronize()
     o_pq, o_pk, o_b, st = oracle.remap(c, q_pos, n_kv)
+    assert np.array_equal(pos_q.cpu().numpy().reshape(3, -1), o_pq)
+    assert np.array_equal(pos_k.cpu().numpy(), o_pk)
+    assert np.array_equal(bounds.cpu().numpy().reshape(3, -1, 2), o_b)
+
+
+PAGE_MODES = [dca.REMAP_PAGE_C, dca.REMAP_PAGE_2C]
+
+
+@pytest.mark.parametrize("mode", PAGE_MODES)
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_remap_page_modes_bit_exact_on_workloads(name, mode):
+    w = synth.WORKLOADS[name]
+    q_pos = (w.q0 + np.arange(w.T, dtype=np.int64)).astype(np.int32)
+    q_pos = np.ascontiguousarray(np.broadcast_to(q_pos, (w.B, w.T)))
+    pos_q, pos_k, bounds = dca.remap_positions(cfg_for(w, remap_mode=mode), to_dev(q_pos), w.N)
+    torch.cuda.synchronize()
+    o_pq, o_pk, o_b, st = oracle.remap(w.chunk, q_pos, w.N, mode=mode)
+    assert st == 0
+    assert np.array_equal(pos_q.cpu().numpy().reshape(3, -1), o_pq)
+    assert np.array_equal(pos_k.cpu().numpy(), o_pk)
+    assert np.array_equal(bounds.cpu().numpy().reshape(3, -1, 2), o_b)
+
+
+@pytest.mark.parametrize("mode", PAGE_MODES)
+@pytest.mark.parametrize("c,n_kv", [(1, 50), (7, 100), (64, 64), (1000, 300), (5, 0)])
+def test_remap_page_modes_edge_positions(c, n_kv, mode):
+    q_pos = np.array([[-5, -1, 0, 1, 6, 7, 8, 49, 63, 64, 99, 100, 299, 300, 1 << 29]], np.int32)
+    cfg = dca.Config(chunk=c, remap_mode=mode)
+    pos_q, pos_k, bounds = dca.remap_positions(cfg, to_dev(q_pos), n_kv)
+    torch.cuda.synchronize()
+    o_pq, o_pk, o_b, st = oracle.remap(c, q_pos, n_kv, mode=mode)
     assert np.array_equal(pos_q.cpu().numpy().reshape(3, -1), o_pq)
     assert np.array_equal(pos_k.cpu().numpy(), o_pk)
     assert np.array_equal(bounds.cpu().numpy().reshape(3, -1, 2), o_b)
@@ -191,6 +224,37 @@ def test_attention_end_to_end(name, n_random, o_dtype):
     o, lse = dca.attention(cfg_for(w, ffd), q, qp, k, o_dtype=o_dtype)
     torch.cuda.synchronize()
     res = _oracle_attention(inp, w, rows=rows, per_regime=False)
+    sel = res["rows"]
+    got_o = o.float().cpu().numpy().reshape(B * T, w.Hq, w.D)[sel]
+    got_l = lse.cpu().numpy().reshape(B * T, w.Hq)[sel]
+    assert_o_close(got_o, res["o"], atol=1e-4 if w.dtype == "f32" else 1e-2)
+    assert_lse_close(got_l, res["lse"], rtol=1e-5 if w.dtype == "f32" else 1e-3)
+
+
+PAGE_E2E = [
+    ("prefill-256-c64-fp32", None, torch.float32),
+    ("prefill-4k-c1024", 32, torch.bfloat16),
+    ("decode-b8-kv256k-c65536", 0, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("mode", PAGE_MODES)
+@pytest.mark.parametrize("name,n_random,o_dtype", PAGE_E2E, ids=[e[0] for e in PAGE_E2E])
+def test_attention_page_modes(name, n_random, o_dtype, mode):
+    """dca_attention under the page-literal remap tables (succ = the whole previous chunk; inter
+    query at c or 2c): the decode row now has a non-empty succ regime of c keys."""
+    inp, w, ffd = _inputs(name)
+    B, T = w.B, w.T
+    if n_random is None:
+        rows = None
+    elif w.T == 1:
+        rows = rows_of(B, T, [(b, 0) for b in range(B)])
+    else:
+        rows = rows_of(B, T, sample_rows(T, w.chunk, n_random, seed=w.seed + mode))
+    q, k, qp = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["q_pos"])
+    o, lse = dca.attention(cfg_for(w, ffd, remap_mode=mode), q, qp, k, o_dtype=o_dtype)
+    torch.cuda.synchronize()
+    res = _oracle_attention(inp, w, rows=rows, per_regime=False, remap_mode=mode)
     sel = res["rows"]
     got_o = o.float().cpu().numpy().reshape(B * T, w.Hq, w.D)[sel]
     got_l = lse.cpu().numpy().reshape(B * T, w.Hq)[sel]
