@@ -120,6 +120,12 @@ AttnWorkspace attention_layout(const dca_config* cfg, dca_dtype dtype, int32_t B
     w.dec_lse = take((size_t)3 * w.n_spans * rows * Hq * 4);
     w.tab_lo = take((size_t)64 * (R / 2) * 8);
     w.tab_hi = take((size_t)w.n_hi * (R / 2) * 8);
+  } else if (dtype == DCA_BF16) {
+    // single fused pass: fp32 rows for O moved out of the registers (regime ends, reference
+    // moves); the final O and lse go straight to the caller's outputs
+    w.o_parts = take(rows * Hq * D * 4);
+    w.lse_parts = take(0);
+    w.dec_o = w.dec_lse = w.tab_lo = w.tab_hi = off;
   } else {
     w.o_parts = take(3 * rows * Hq * D * 4);
     w.lse_parts = take(3 * rows * Hq * 4);
@@ -425,6 +431,18 @@ dca_status dca_attention(const dca_config* cfg, dca_dtype dtype, int32_t B, int3
   a.k_rot_hs = R;
   float* op = (float*)(ws + L.o_parts);
   float* lp = (float*)(ws + L.lse_parts);
+  if (dtype == DCA_BF16) {
+    // one pass over the three regimes under one online softmax: no partials, no merge
+    a.fused = 1;
+    a.o[0] = op;
+    a.o_final = o;
+    a.o_final_bf16 = o_dtype == DCA_BF16;
+    a.lse_final = lse;
+    if ((st = hip_status(dca::launch_attn_prefill_bf16(a, stream), "prefill attention launch")))
+      return st;
+    if ((st = hip_status(mark(4, stream), "stage event"))) return st;
+    return hip_status(mark(5, stream), "stage event");
+  }
   for (int r = 0; r < 3; ++r) {
     a.o[r] = op + (size_t)r * rows * Hq * D;
     a.lse[r] = lp + (size_t)r * rows * Hq;
