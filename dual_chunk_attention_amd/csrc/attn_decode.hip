@@ -27,7 +27,6 @@ constexpr int kTile = 64;
 constexpr int kTileBytes = kTile * kD * 2;   // 64 KiB
 constexpr float kTau = 8.0f;
 
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 // 16-byte chunk swizzle of a tile row, conflict-free on gfx950 (256-byte bank window) for the
@@ -50,9 +49,13 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(DecodeArgs da) {
   const AttnArgs& a = da.base;
   __shared__ __attribute__((aligned(1024))) char kbuf[2 * kTileBytes];
   __shared__ __attribute__((aligned(16))) bf16 pbuf[16 * kTile];     // P[head][key]
+  __shared__ __attribute__((aligned(1024))) float2 hbuf[2][128];      // hi table row of a tile
   __shared__ float smax[4][16], ssum[4][16], wsum[4][16];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int wu = __builtin_amdgcn_readfirstlane(w);   // the wave index in a scalar register
+  const uint32_t kbuf_lds = (uint32_t)(uintptr_t)(lds_char*)kbuf;
+  const uint32_t hbuf_lds = (uint32_t)(uintptr_t)(lds_char*)&hbuf[0][0];
   const int hcol = l & 15, gq = l >> 4;   // column (query head) and 16-lane group
   const int G = a.Hq / a.Hkv;
   const int64_t rows = (int64_t)a.B * a.T;
@@ -90,6 +93,20 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(DecodeArgs da) {
   // PV operand (transpose read): rows 32 ks + 8 gq + 4 e + j/4, dims 128 w + 16 dt + 4 (j%4).
   const int j16 = l & 15;
 
+  // Key rotation from the tables.  With c a multiple of 64, the 64 keys of an aligned tile sit at
+  // positions p0 + row (p0 = k0 mod c, a multiple of 64): the lane's lo entries (row qrow) are the
+  // same for every tile and stay in registers, and the tile's single hi row travels to LDS with
+  // the tile's loads.  Other chunk sizes read both tables per key.
+  const bool tab_tile = ROTATE && da.chunk % 64 == 0;
+  const int n_hi = (da.chunk + 63) / 64;
+  float2 lo_q[16];
+  if (tab_tile) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lo_q[8 * s + e] = da.rot_lo[qrow * half_rot + 32 * s + 8 * gq + e];
+  }
+
   for (int r = 0; r < 3; ++r) {
     if (!(da.regime_mask & (1 << r))) continue;
     const int slot = da.slot0[r] + span;
@@ -117,20 +134,27 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(DecodeArgs da) {
     float m_used = -INFINITY, l_part = 0.0f, w_part = 0.0f;
 
     const int kt0 = lo / kTile, kt1 = hi / kTile;
+    // tile k0..k0+63 by direct global->LDS loads: wave w fills rows 16w..16w+15, lane l the
+    // physical chunk l of a row with logical chunk l ^ swz(row); rows past the cache re-read its
+    // last key (their scores are masked)
     auto issue = [&](int buf, int k0) {
-      char* base = kbuf + buf * kTileBytes;
+      const uint32_t base = kbuf_lds + buf * kTileBytes;
+      const int64_t key_bytes = (int64_t)a.Hkv * kD * 2;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int row = 16 * w + i;
+        const int row = 16 * wu + i;
         int key = k0 + row;
         key = min(max(key, 0), a.n_kv - 1);
-        const int c = l ^ swz(row);
-        __builtin_amdgcn_global_load_lds(kraw_b + (int64_t)key * a.Hkv * kD + 8 * c,
-                                         (lds_void*)(base + row * 1024), 16, 0, 0);
+        const char* src = uniform_ptr((const char*)kraw_b + (int64_t)key * key_bytes);
+        dma16(src + 16 * (l ^ swz(row)), base + row * 1024);
+      }
+      if (tab_tile && wu == 0) {   // hi row of the tile (lanes 32..63 fetch the next row, unused)
+        const int hr = min((int)((int64_t)k0 % da.chunk >> 6) + (l >> 5), n_hi - 1);
+        dma16(da.rot_hi + (int64_t)hr * half_rot + 2 * (l & 31), hbuf_lds + buf * 1024);
       }
     };
     issue(0, kt0 * kTile);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vm0();
     __syncthreads();
 
     for (int kt = kt0; kt <= kt1; ++kt) {
@@ -145,27 +169,37 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(DecodeArgs da) {
 #pragma unroll
       for (int s = 0; s < 16; ++s) kf[s] = *(const bf16x8*)(kb + qk_off[s & 3] + 256 * (s >> 2));
       if (ROTATE) {
-        const int64_t pos = (int64_t)min(key, a.n_kv - 1) % da.chunk;
-        const float2* tlo = da.rot_lo + (pos & 63) * half_rot;
-        const float2* thi = da.rot_hi + (pos >> 6) * half_rot;
+        // rotate the rotary pairs (f, f + 64) of the lane's key by (cos, sin) of pos * w_f,
+        // composed from the lo and hi tables by the angle-addition formulas
+        auto rotate = [&](auto lo_of, auto hi_of) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
+          for (int s = 0; s < 2; ++s) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int f = 32 * s + 8 * gq + e;
-            const float2 A = tlo[f], Bv = thi[f];
-            const float cs = A.x * Bv.x - A.y * Bv.y;
-            const float sn = A.y * Bv.x + A.x * Bv.y;
-            const float x0 = (float)kf[s][e], x1 = (float)kf[s + 2][e];
-            const float y0 = fmaf(x0, cs, -x1 * sn), y1 = fmaf(x0, sn, x1 * cs);
-            if constexpr (ROT16) {
-              kf[s][e] = __builtin_bit_cast(bf16, (f16)y0);
-              kf[s + 2][e] = __builtin_bit_cast(bf16, (f16)y1);
-            } else {
-              kf[s][e] = (bf16)y0;
-              kf[s + 2][e] = (bf16)y1;
+            for (int e = 0; e < 8; ++e) {
+              const int f = 32 * s + 8 * gq + e;
+              const float2 A = lo_of(8 * s + e, f), Bv = hi_of(f);
+              const float cs = A.x * Bv.x - A.y * Bv.y;
+              const float sn = A.y * Bv.x + A.x * Bv.y;
+              const float x0 = (float)kf[s][e], x1 = (float)kf[s + 2][e];
+              const float y0 = fmaf(x0, cs, -x1 * sn), y1 = fmaf(x0, sn, x1 * cs);
+              if constexpr (ROT16) {
+                kf[s][e] = __builtin_bit_cast(bf16, (f16)y0);
+                kf[s + 2][e] = __builtin_bit_cast(bf16, (f16)y1);
+              } else {
+                kf[s][e] = (bf16)y0;
+                kf[s + 2][e] = (bf16)y1;
+              }
             }
           }
+        };
+        if (tab_tile) {
+          const float2* th = &hbuf[cur][0];
+          rotate([&](int i, int) { return lo_q[i]; }, [&](int f) { return th[f]; });
+        } else {
+          const int64_t pos = (int64_t)min(key, a.n_kv - 1) % da.chunk;
+          const float2* tlo = da.rot_lo + (pos & 63) * half_rot;
+          const float2* thi = da.rot_hi + (pos >> 6) * half_rot;
+          rotate([&](int, int f) { return tlo[f]; }, [&](int f) { return thi[f]; });
         }
       } else {
         const bf16* kr = krot_b + (int64_t)min(key, a.n_kv - 1) * a.Hkv * a.k_rot_hs + 8 * gq;  // 2-byte elements
@@ -235,7 +269,7 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(DecodeArgs da) {
           o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb, o[dt], 0, 0, 0);
         }
       }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      wait_vm0();
       __syncthreads();
     }
 

@@ -44,7 +44,6 @@ constexpr int kVloBytes = kNK * kRot * 2;        // 8 KiB
 constexpr int kStageBytes = kKqkBytes + kVloBytes;
 constexpr float kTau = 64.0f;                    // reference-move threshold (log2 units)
 
-typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 // 16-byte chunk swizzle of a tile row (gfx950 LDS conflicts within 256-byte windows): rows
@@ -52,31 +51,6 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 // and rows 4k..4k+3 map a chunk pair to distinct 32-byte slots (the 32-lane transpose reads).
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
-// 16-byte global->LDS load: lane l's bytes land at LDS address lds_row_addr + 16 l.  Issued as inline asm
-// on purpose: the compiler's wait-count model charges these loads to the LDS counter as well, so
-// every LDS-read wait inside the tile loop would also wait for the next tile's loads to arrive
-// from memory.  The kernel orders them itself (s_waitcnt vmcnt + barrier before a stage is read),
-// and no other instruction of the kernel uses M0.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_row_addr) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_row_addr);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// a wave-uniform pointer, placed in scalar registers
-__device__ __forceinline__ const char* uniform_ptr(const char* p) {
-  const uint64_t v = (uint64_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (const char*)(((uint64_t)hi << 32) | lo);
-}
-
-// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left open) through the builtin, so that the compiler's
-// own wait placement knows that every earlier global load has completed
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // LDS fragments in flight ahead of the MFMA that consumes them (S^T and O^T products)
 constexpr int kDepthK = 4;

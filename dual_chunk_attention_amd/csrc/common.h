@@ -33,6 +33,35 @@ __device__ __forceinline__ int64_t floordiv64(int64_t a, int64_t b) {
 }
 
 // Wave-wide reductions over 64 lanes (fixed butterfly order, so results are deterministic).
+typedef __attribute__((address_space(3))) char lds_char;
+
+// 16-byte global->LDS load: lane l's bytes land at LDS address lds_row_addr + 16 l (the address
+// must be wave-uniform).  Issued as inline asm on purpose: the compiler's wait-count model charges
+// these loads to the LDS counter as well, so every LDS-read wait inside a tile loop would also
+// wait for the next tile's loads to arrive from memory.  A kernel using it orders the loads
+// itself (wait_vm0 + barrier before a stage is read), and no other instruction of the attention
+// kernels uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_row_addr) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_row_addr);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// a wave-uniform pointer, placed in scalar registers
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(((uint64_t)hi << 32) | lo);
+}
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left open) through the builtin, so that the compiler's
+// own wait placement knows that every earlier global load has completed
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
