@@ -225,8 +225,8 @@ def main():
                    "heads_q": w.Hq, "heads_kv": w.Hkv, "head_dim": w.D, "n_rot": w.n_rot},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": measured_traffic("attn_prefill.hip") if w.name == "prefill-32k-c8192" else None,
-                     "kernel": "attn_prefill_kernel (3 regime passes, one launch)",
+                     "traffic": measured_traffic("attn_fused.hip") if w.name == "prefill-32k-c8192" else None,
+                     "kernel": "attn_fused_kernel (the three regimes in one pass, one launch)",
                      "kernel_ms": attn_ms, "algorithmic_flop": flops},
         "stages_ms": {"remap": stages[0], "rope_q": stages[1], "rope_k": stages[2],
                       "regime_passes": stages[3], "merge": stages[4]},

@@ -438,7 +438,7 @@ dca_status dca_attention(const dca_config* cfg, dca_dtype dtype, int32_t B, int3
     a.o_final = o;
     a.o_final_bf16 = o_dtype == DCA_BF16;
     a.lse_final = lse;
-    if ((st = hip_status(dca::launch_attn_prefill_bf16(a, stream), "prefill attention launch")))
+    if ((st = hip_status(dca::launch_attn_fused_bf16(a, stream), "prefill attention launch")))
       return st;
     if ((st = hip_status(mark(4, stream), "stage event"))) return st;
     return hip_status(mark(5, stream), "stage event");

@@ -68,7 +68,7 @@ __device__ __forceinline__ f32x16 mfma_rot(const bf16x8& a, const bf16x8& b, con
   }
 }
 
-template <int G, bool ROT16, bool FUSED>
+template <int G, bool ROT16>
 __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_qblocks) {
   constexpr int QB = 128 / G;  // query positions per workgroup
   __shared__ __attribute__((aligned(1024))) char smem[2 * kStageBytes];
@@ -138,22 +138,8 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
 
   // per-regime pointers without indexing the argument arrays at run time
   auto o_of = [&](int r) { return r == 0 ? a.o[0] : r == 1 ? a.o[1] : a.o[2]; };
-  // the last regime with keys for this workgroup (fused pass: O stays in registers through it)
-  int r_last = -1;
-  if (FUSED) {
-    for (int r = 0; r < 3; ++r)
-      for (int p = 0; p < QB; ++p)
-        if (s_lo[r][p] <= s_hi[r][p]) r_last = r;
-  }
-  // Online-softmax state of the lane's row.  Separate passes: per regime.  Fused pass: the
-  // reference, sums and the flushed part run on through the three regimes; O is moved into the
-  // fp32 scratch rows (o[0]) at the end of every regime but the last with keys, exactly like a
-  // reference move with alpha = 1, so it never has to stay in registers across regimes.
-  float m_used = -INFINITY, l_part = 0.0f, w_part = 0.0f;
-  bool flushed = false;
-
   for (int r = 0; r < 3; ++r) {
-    if (!FUSED && !a.o[r]) continue;
+    if (!a.o[r]) continue;
     // union of the rows' intervals and the range where no row needs masking
     int umin = 0x7fffffff, umax = -1, fmax_lo = -0x7fffffff, fmin_hi = 0x7fffffff;
     for (int p = 0; p < QB; ++p) {
@@ -175,16 +161,13 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
     f32x16 o[16];
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt) o[dt] = f32x16{};
-    // l_part: sum of the exact p (for the LSE); w_part: sum of the bf16-rounded p that the PV
-    // product uses (O is normalised by it, so a dominant key's value comes out exactly)
-    if (!FUSED) {
-      m_used = -INFINITY;
-      l_part = 0.0f;
-      w_part = 0.0f;
-      flushed = false;
-    }
-    // fp32 rows that take O out of the registers: the regime's own output, or the scratch rows
-    float* const frow = o_of(FUSED ? 0 : r) + rowhead * kD + 4 * half;
+    // online-softmax state of the lane's row.  l_part: sum of the exact p (for the LSE); w_part:
+    // sum of the bf16-rounded p that the PV product uses (O is normalised by it, so a dominant
+    // key's value comes out exactly)
+    float m_used = -INFINITY, l_part = 0.0f, w_part = 0.0f;
+    bool flushed = false;
+    // the regime's fp32 output rows, which also take O out of the registers on a reference move
+    float* const frow = o_of(r) + rowhead * kD + 4 * half;
 
     if (umin <= umax) {
       const int kt0 = max(umin, 0) / kNK, kt1 = min(umax, a.n_kv - 1) / kNK;
@@ -370,30 +353,6 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
     }
 
     // ---- end of the regime -----------------------------------------------------------------
-    if (FUSED) {
-      // O leaves the registers unless this is the workgroup's last regime with keys
-      if (r != r_last) {
-        if (umin <= umax && row_valid && m_used != -INFINITY) {
-#pragma unroll
-          for (int dt = 0; dt < 16; ++dt) {
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-              f32x4 v;
-              v[0] = o[dt][4 * q4 + 0];
-              v[1] = o[dt][4 * q4 + 1];
-              v[2] = o[dt][4 * q4 + 2];
-              v[3] = o[dt][4 * q4 + 3];
-              f32x4* dst = (f32x4*)(frow + 32 * dt + 8 * q4);
-              if (flushed) v += *dst;
-              *dst = v;
-            }
-          }
-          flushed = true;
-          wait_vm0();   // read back by the next flush or the final epilogue
-        }
-        continue;
-      }
-    }
     // normaliser and natural-log lse from the row totals of both halves of the wave
     float l_tot, w_tot;
     {
@@ -408,8 +367,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
     const float inv = nonempty ? 1.0f / w_tot : 0.0f;
     const float lse = nonempty ? (m_used + log2f(l_tot)) * kLn2 : -INFINITY;
     if (row_valid) {
-      // separate pass: this regime's normalised fp32 partial; fused pass: the final O, bf16 or
-      // fp32, of all three regimes
+      // this regime's normalised fp32 partial
 #pragma unroll
       for (int dt = 0; dt < 16; ++dt) {
 #pragma unroll
@@ -422,46 +380,11 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(AttnArgs a, int n_
           f32x4* src = (f32x4*)(frow + 32 * dt + 8 * q4);
           if (flushed) v += *src;
           v *= inv;
-          if (!FUSED) {
-            *src = v;
-          } else {
-            const int64_t at = rowhead * kD + 32 * dt + 8 * q4 + 4 * half;
-            if (a.o_final_bf16) {
-              bf16x4 vb;
-              vb[0] = (bf16)v[0];
-              vb[1] = (bf16)v[1];
-              vb[2] = (bf16)v[2];
-              vb[3] = (bf16)v[3];
-              *(bf16x4*)((bf16*)a.o_final + at) = vb;
-            } else {
-              *(f32x4*)((float*)a.o_final + at) = v;
-            }
-          }
+          *src = v;
         }
       }
-      if (half == 0) {
-        if (!FUSED)
-          a.lse[r][rowhead] = lse;
-        else
-          a.lse_final[rowhead] = lse;
-      }
+      if (half == 0) a.lse[r][rowhead] = lse;
     }
-    if (FUSED) break;   // the last regime with keys
-  }
-  // fused pass of a workgroup none of whose rows has a key: O = 0, lse = -inf
-  if (FUSED && r_last < 0 && row_valid) {
-#pragma unroll
-    for (int c16 = 0; c16 < 16; ++c16) {
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int64_t at = rowhead * kD + 32 * c16 + 8 * q4 + 4 * half;
-        if (a.o_final_bf16)
-          *(bf16x4*)((bf16*)a.o_final + at) = bf16x4{};
-        else
-          *(f32x4*)((float*)a.o_final + at) = f32x4{};
-      }
-    }
-    if (half == 0) a.lse_final[rowhead] = -INFINITY;
   }
 }
 
@@ -475,12 +398,7 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)blocks), block(256);
 #define DCA_PREFILL_LAUNCH(GG)                                                                   \
   case GG:                                                                                       \
-    if (a.fused)                                                                                 \
-      hipLaunchKernelGGL((attn_prefill_kernel<GG, ROT16, true>), grid, block, 0, stream, a,      \
-                         n_qblocks);                                                             \
-    else                                                                                         \
-      hipLaunchKernelGGL((attn_prefill_kernel<GG, ROT16, false>), grid, block, 0, stream, a,     \
-                         n_qblocks);                                                             \
+    hipLaunchKernelGGL((attn_prefill_kernel<GG, ROT16>), grid, block, 0, stream, a, n_qblocks);  \
     break;
   switch (G) {
     DCA_PREFILL_LAUNCH(1)

@@ -32,7 +32,6 @@ __device__ __forceinline__ int64_t floordiv64(int64_t a, int64_t b) {
   return q;
 }
 
-// Wave-wide reductions over 64 lanes (fixed butterfly order, so results are deterministic).
 typedef __attribute__((address_space(3))) char lds_char;
 
 // 16-byte global->LDS load: lane l's bytes land at LDS address lds_row_addr + 16 l (the address
@@ -62,6 +61,7 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
 // own wait placement knows that every earlier global load has completed
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Wave-wide reductions over 64 lanes (fixed butterfly order, so results are deterministic).
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -154,6 +154,9 @@ hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
 
 // bf16 prefill regime passes with MFMA; D = 512, n_rot = 128, Hq/Hkv in {1,2,4,8,16,32}.
 hipError_t launch_attn_prefill_bf16(const AttnArgs& a, hipStream_t stream);
+// bf16 prefill, the three regimes in one pass (a.fused set, fp16 rotary operands); D = 512,
+// n_rot = 128, Hq/Hkv in {1,2,4,8,16}.
+hipError_t launch_attn_fused_bf16(const AttnArgs& a, hipStream_t stream);
 
 // bf16 split-KV decode passes.  Each (b,t,g, span of `span` keys, regime r) emits one partial
 // into part slot slot0[r] + span: o_part [slot][B*T*Hq][D], lse_part [slot][B*T*Hq].
