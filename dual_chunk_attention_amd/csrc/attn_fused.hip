@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
   __syncthreads();
 
   // ---- the tile sequence: regimes 0, 1, 2, each over the union of its rows' intervals --------
-  int st[3], kt0[3], full_lo[3], full_hi[3], my_lo[3], my_hi[3];
+  int st[3], kt0[3], full_lo[3], full_hi[3];
   int n_tiles = 0;
 #pragma unroll
   for (int r = 0; r < 3; ++r) {
@@ -156,8 +156,6 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
       fmax_lo = max(fmax_lo, lo);
       fmin_hi = min(fmin_hi, hi);
     }
-    my_lo[r] = s_lo[r][pos_in_blk];
-    my_hi[r] = s_hi[r][pos_in_blk];
     const int k_first = umin <= umax ? umin / kNK : 0;
     const int cnt = umin <= umax ? umax / kNK - k_first + 1 : 0;
     st[r] = __builtin_amdgcn_readfirstlane(n_tiles);
@@ -168,12 +166,13 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
     n_tiles += cnt;
   }
   n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
-  auto regime_of = [&](int i) { return i >= st[2] ? 2 : (i >= st[1] ? 1 : 0); };
-  auto pick = [&](const int* v, int r) { return r == 2 ? v[2] : r == 1 ? v[1] : v[0]; };
-  auto k0_of = [&](int i) {
-    const int r = regime_of(i);
-    return (pick(kt0, r) + i - pick(st, r)) * kNK;
-  };
+  // per-tile lookups as scalar selects on the tile index (no indexing of the per-regime arrays,
+  // which the compiler would turn into chains of branches)
+  const int st1 = st[1], st2 = st[2];
+  auto sel = [&](int i, int v0, int v1, int v2) { return i >= st2 ? v2 : (i >= st1 ? v1 : v0); };
+  auto regime_of = [&](int i) { return (int)(i >= st1) + (int)(i >= st2); };
+  const int kb0 = kt0[0] * kNK, kb1 = (kt0[1] - st1) * kNK, kb2 = (kt0[2] - st2) * kNK;
+  auto k0_of = [&](int i) { return sel(i, kb0, kb1, kb2) + kNK * i; };
   auto load_qrot = [&](int r) {
     const void* base = r == 0 ? a.q_rot[0] : r == 1 ? a.q_rot[1] : a.q_rot[2];
     const bf16* qr = (const bf16*)base + rowhead * a.q_rot_hs + 8 * half;
@@ -260,13 +259,15 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
   // without any valid key so far has m = -inf and only masked scores, so any finite reference gives
   // the same zeros.  The exponents are <= kTau, so the raw v_exp_f32 suffices.  psum: the exact p;
   // wsum: the bf16-rounded p that the PV product uses (exact products by one).
-  auto exp_pair = [&](const float* sv, int e, float neg_m, bf16x8* pk, float& psum, float& wsum) {
+  // Sums go to partial accumulators (psum[e/2 % 4], wsum[e/2 % 2]) so that the adds do not form
+  // one long dependent chain (one wave per SIMD exposes every VALU latency).
+  auto exp_pair = [&](const float* sv, int e, float neg_m, bf16x8* pk, float* psum, float* wsum) {
     const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], scale_log2, neg_m));
     const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e + 1], scale_log2, neg_m));
     const bf16x2 pb = {(bf16)p0, (bf16)p1};
-    psum += p0;
-    psum += p1;
-    wsum = __builtin_amdgcn_fdot2_f32_bf16(pb, bf16x2{(bf16)1.0f, (bf16)1.0f}, wsum, false);
+    psum[(e >> 1) & 3] += p0 + p1;
+    wsum[(e >> 1) & 1] =
+        __builtin_amdgcn_fdot2_f32_bf16(pb, bf16x2{(bf16)1.0f, (bf16)1.0f}, wsum[(e >> 1) & 1], false);
     pk[e >> 3][e & 7] = pb[0];
     pk[e >> 3][(e & 7) + 1] = pb[1];
   };
@@ -275,20 +276,24 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
   // row (the first tile with a valid key sets it, O of the row being still 0; a tile more than
   // kTau above it moves it), and the probabilities of keys 0..15 of the tile (pk[0]).  Returns the
   // factor (1 unless the reference moved) by which the O accumulated so far must be scaled.
-  auto softmax_head = [&](float* sv, int i, bf16x8* pk, float& neg_m, float& psum, float& wsum) {
-    const int r = regime_of(i), k0 = k0_of(i);
-    if (!(pick(full_lo, r) <= k0 && k0 + kNK - 1 <= pick(full_hi, r))) {
-      const int lo_eff = pick(my_lo, r) - k0, hi_eff = pick(my_hi, r) - k0;
+  auto softmax_head = [&](float* sv, int i, bf16x8* pk, float& neg_m, float* psum, float* wsum) {
+    const int k0 = k0_of(i);
+    if (!(sel(i, full_lo[0], full_lo[1], full_lo[2]) <= k0 &&
+          k0 + kNK - 1 <= sel(i, full_hi[0], full_hi[1], full_hi[2]))) {
+      const int r = regime_of(i);
+      const int lo_eff = s_lo[r][pos_in_blk] - k0, hi_eff = s_hi[r][pos_in_blk] - k0;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int kk = 8 * (e >> 2) + 4 * half + (e & 3);
         if (kk < lo_eff || kk > hi_eff) sv[e] = -INFINITY;
       }
     }
-    float mx = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
+    // row maximum as a tree (depth 3 of 3-input maxima)
+    float m6[6];
 #pragma unroll
-    for (int e = 3; e < 15; e += 2) mx = fmaxf(fmaxf(mx, sv[e]), sv[e + 1]);
-    mx = fmaxf(mx, sv[15]);
+    for (int k = 0; k < 5; ++k) m6[k] = fmaxf(fmaxf(sv[3 * k], sv[3 * k + 1]), sv[3 * k + 2]);
+    m6[5] = sv[15];
+    float mx = fmaxf(fmaxf(fmaxf(m6[0], m6[1]), m6[2]), fmaxf(fmaxf(m6[3], m6[4]), m6[5]));
     {
       auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       mx = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1])) * scale_log2;
@@ -300,8 +305,9 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
     l_part *= alpha;
     w_part *= alpha;
     neg_m = m_used == -INFINITY ? 0.0f : -m_used;
-    psum = 0.0f;
-    wsum = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) psum[k] = 0.0f;
+    wsum[0] = wsum[1] = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; e += 2) exp_pair(sv, e, neg_m, pk, psum, wsum);
     return alpha;
@@ -357,7 +363,7 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
 #pragma unroll
     for (int e = 0; e < 16; ++e) sv[e] = acc[e];
     bf16x8 pk[2];
-    float neg_m, psum, wsum;
+    float neg_m, psum[4], wsum[2];
     const float alpha = softmax_head(sv, i, pk, neg_m, psum, wsum);
     // the reference of some rows moved: O (tiles up to i-1) of the wave's rows is moved, rescaled,
     // into their fp32 scratch rows and restarts at zero before tile i adds in (rescaling the 256
@@ -390,8 +396,8 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
     values(off_c, pk, [&](int j) {
       if (j < 12 && j % 3 == 1) exp_pair(sv, 8 + 2 * (j / 3), neg_m, pk, psum, wsum);
     });
-    l_part += psum;
-    w_part += wsum;
+    l_part += (psum[0] + psum[1]) + (psum[2] + psum[3]);
+    w_part += wsum[0] + wsum[1];
     const int t_off = off_c;
     off_c = off_n;
     off_n = off_d;
