@@ -3,7 +3,8 @@
 One step = one dca_attention call (remap, query rotation x3, key rotation, the three regime passes,
 the N-way merge) on the 32k-token prefill workload (one global layer: 16 query heads, 2 KV heads,
 head_dim 512, chunk 8192, bf16, inputs resident in HBM).  The 256k-KV decode workload (8 sequences,
-chunk 65536) is timed as a second leg.  Prints one JSON line.
+chunk 65536) is timed as a second leg, and the same decode over a q8_0 key cache as a third.  Prints
+one JSON line.
 
 value: query tokens per second of the prefill workload.  roofline: the regime-pass kernel, timed
 live with HIP events recorded by the library between its stages, against the bf16 MFMA peak
@@ -70,23 +71,33 @@ def to_dev(torch, a):
 
 def algorithmic_work(w):
     """Prefill: 4*D*Hq FLOP per attended (query, key) pair (QK^T and PV, every pair once across
-    the three regimes).  Decode: B*N*Hkv*D*2 bytes (the cache read once; K = V)."""
+    the three regimes).  Decode: the cache read once (K = V): B*N*Hkv*D*2 bytes for bf16,
+    B*N*Hkv*(D + 2*D/32) for q8_0 (one int8 code per dim, one fp16 scale per 32 dims)."""
     i = w.q0 + np.arange(w.T, dtype=np.float64)
     pairs = float(np.minimum(i + 1, w.N).sum()) * w.B
     flops = 4.0 * w.D * w.Hq * pairs
-    kv_bytes = float(w.B) * w.N * w.Hkv * w.D * 2
+    row_bytes = w.D + 2 * (w.D // 32) if w.dtype == "q8_0" else w.D * 2
+    kv_bytes = float(w.B) * w.N * w.Hkv * row_bytes
     return flops, kv_bytes
 
 
 def time_leg(torch, dca, w, inp, steps, warmup):
     cfg = dca.Config(head_dim=w.D, n_rot=w.n_rot, n_head_q=w.Hq, n_head_kv=w.Hkv, chunk=w.chunk,
                      rope_theta=w.theta, scale=w.scale, freq_factors=to_dev(torch, inp["freq_factors"]))
-    q, k, qp = to_dev(torch, inp["q"]), to_dev(torch, inp["k"]), to_dev(torch, inp["q_pos"])
-    ws = torch.empty(dca.attention_workspace_size(cfg, q.dtype, w.B, w.T, w.N), dtype=torch.uint8, device="cuda:0")
+    q, qp = to_dev(torch, inp["q"]), to_dev(torch, inp["q_pos"])
+    if w.dtype == "q8_0":
+        k = (to_dev(torch, inp["k_codes"]), to_dev(torch, inp["k_scales"].view(np.int16)))
+        ws_bytes = dca.attention_q8_workspace_size(cfg, w.B, w.T, w.N)
+        call = dca.attention_q8
+    else:
+        k = (to_dev(torch, inp["k"]),)
+        ws_bytes = dca.attention_workspace_size(cfg, q.dtype, w.B, w.T, w.N)
+        call = dca.attention
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda:0")
     out = torch.empty((w.B, w.T, w.Hq, w.D), dtype=torch.bfloat16, device="cuda:0")
     lse = torch.empty((w.B, w.T, w.Hq), dtype=torch.float32, device="cuda:0")
     for _ in range(warmup):
-        dca.attention(cfg, q, qp, k, workspace=ws, out=out, lse=lse)
+        call(cfg, q, qp, *k, workspace=ws, out=out, lse=lse)
     torch.cuda.synchronize()
     ev = HipEvents(6 * steps)
     start = torch.cuda.Event(enable_timing=True)
@@ -96,7 +107,7 @@ def time_leg(torch, dca, w, inp, steps, warmup):
     for s in range(steps):
         sub = (ctypes.c_void_p * 6)(*ev.arr[6 * s:6 * s + 6])
         dca.set_stage_events(sub)
-        dca.attention(cfg, q, qp, k, workspace=ws, out=out, lse=lse)
+        call(cfg, q, qp, *k, workspace=ws, out=out, lse=lse)
     end.record()
     dca.set_stage_events(None)
     torch.cuda.synchronize()
@@ -187,6 +198,8 @@ def main():
     ap.add_argument("--workload", default="prefill-32k-c8192")
     ap.add_argument("--decode-workload", default="decode-b8-kv256k-c65536")
     ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--q8-workload", default="decode-b8-kv256k-c65536-q8")
+    ap.add_argument("--no-q8", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -250,6 +263,24 @@ def main():
                           "regime_passes": std[3], "merge": std[4]},
         }
         del inpd
+    if not args.no_q8:
+        wq = synth.WORKLOADS[args.q8_workload]
+        inpq = synth.make_inputs(wq)
+        msq, stq = time_leg(torch, dca, wq, inpq, args.decode_steps, args.warmup)
+        _, q8_bytes = algorithmic_work(wq)
+        gbps = q8_bytes / (stq[3] * 1e-3) / 1e9
+        rec["decode_q8"] = {
+            "workload": wq.name, "value": wq.B * wq.T / (msq * 1e-3), "unit": "tokens/s",
+            "ms_per_step": msq, "steps": args.decode_steps,
+            "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": gbps / HBM_PEAK_GBPS,
+                         "traffic": measured_traffic("attn_decode_q8.hip") if wq.name == "decode-b8-kv256k-c65536-q8" else None,
+                         "kernel": "attn_decode_q8_kernel (split-KV over the q8_0 cache, 3 regimes)",
+                         "kernel_ms": stq[3], "algorithmic_bytes": q8_bytes},
+            "stages_ms": {"remap": stq[0], "rope_q": stq[1], "tables": stq[2],
+                          "regime_passes": stq[3], "merge": stq[4]},
+        }
+        del inpq
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0").fill_(1.0)
         dst = torch.empty_like(src)
@@ -266,6 +297,10 @@ def main():
             rd = rec["decode"]["roofline"]
             rd["measured_peak"] = pk["hbm_read_gbps"]
             rd["frac_of_measured_peak"] = rd["achieved"] / pk["hbm_read_gbps"]
+        if "decode_q8" in rec:
+            rq = rec["decode_q8"]["roofline"]
+            rq["measured_peak"] = pk["hbm_read_gbps"]
+            rq["frac_of_measured_peak"] = rq["achieved"] / pk["hbm_read_gbps"]
         rec["measured_peaks"] = pk
     if not args.no_cpu_baseline:
         inp = synth.make_inputs(w)

@@ -95,7 +95,7 @@ struct AttnWorkspace {
 };
 
 AttnWorkspace attention_layout(const dca_config* cfg, dca_dtype dtype, int32_t B, int32_t T,
-                               int32_t n_kv) {
+                               int32_t n_kv, bool split_kv = false) {
   AttnWorkspace w{};
   const size_t rows = (size_t)B * T;
   const size_t es = elem_size(dtype);
@@ -109,7 +109,7 @@ AttnWorkspace attention_layout(const dca_config* cfg, dca_dtype dtype, int32_t B
   w.pos_q = take(3 * rows * 4);
   w.bounds = take(3 * rows * 2 * 4);
   w.qrot = take(3 * rows * Hq * R * es);   // bf16 path: fp16, same size
-  const bool dec = use_decode(dtype, T);
+  const bool dec = split_kv || use_decode(dtype, T);
   w.krot = take(dec ? 0 : (size_t)B * n_kv * Hkv * R * es);
   if (dec) {
     decode_split(n_kv, &w.span, &w.n_spans);
@@ -464,6 +464,88 @@ dca_status dca_attention(const dca_config* cfg, dca_dtype dtype, int32_t B, int3
   m.o_out = o;
   m.lse_out = lse;
   if ((st = hip_status(dca::launch_merge(m, o_dtype == DCA_BF16, stream), "merge launch"))) return st;
+  return hip_status(mark(5, stream), "stage event");
+}
+
+size_t dca_attention_q8_workspace_size(const dca_config* cfg, int32_t B, int32_t T, int32_t n_kv) {
+  if (check_config(cfg, DCA_BF16) || check_sizes(B, T, n_kv)) return 0;
+  return attention_layout(cfg, DCA_BF16, B, T, n_kv, true).total;
+}
+
+dca_status dca_attention_q8(const dca_config* cfg, int32_t B, int32_t T, const void* q,
+                            const int32_t* q_pos, const int8_t* k_codes, const uint16_t* k_scales,
+                            int32_t n_kv, dca_dtype o_dtype, void* o, float* lse, void* workspace,
+                            size_t ws_bytes, hipStream_t stream) {
+  dca_status st = check_config(cfg, DCA_BF16);
+  if (st) return st;
+  if ((st = check_sizes(B, T, n_kv))) return st;
+  if (!valid_dtype(o_dtype)) return fail(DCA_ERR_INVALID_ARGUMENT, "unknown o_dtype %d", (int)o_dtype);
+  const int64_t rows = (int64_t)B * T;
+  if (rows == 0) return DCA_OK;
+  if (!q || !q_pos || !o || (n_kv > 0 && (!k_codes || !k_scales)))
+    return fail(DCA_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (rows * cfg->n_head_kv > 65535) return fail(DCA_ERR_UNSUPPORTED, "batch too large for the split-KV path");
+  const AttnWorkspace L = attention_layout(cfg, DCA_BF16, B, T, n_kv, true);
+  if (ws_bytes < L.total || !workspace)
+    return fail(DCA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", ws_bytes, L.total);
+  char* ws = (char*)workspace;
+  int32_t* pos_q = (int32_t*)(ws + L.pos_q);
+  int32_t* bounds = (int32_t*)(ws + L.bounds);
+  void* qrot = ws + L.qrot;
+  const int64_t Hq = cfg->n_head_q, R = cfg->n_rot, D = cfg->head_dim;
+
+  if ((st = hip_status(mark(0, stream), "stage event"))) return st;
+  if ((st = hip_status(dca::launch_remap(q_pos, rows, cfg->chunk, cfg->remap_mode, n_kv, pos_q, nullptr, bounds, stream),
+                       "remap launch")))
+    return st;
+  if ((st = hip_status(mark(1, stream), "stage event"))) return st;
+  dca::RopeArgs rq = rope_args_for_q(cfg, q, rows, qrot, pos_q);
+  if ((st = hip_status(dca::launch_rope(rq, true, stream), "rope(q) launch"))) return st;
+  if ((st = hip_status(mark(2, stream), "stage event"))) return st;
+  float2* lo = (float2*)(ws + L.tab_lo);
+  float2* hi = (float2*)(ws + L.tab_hi);
+  if ((st = hip_status(dca::launch_rope_tables(lo, hi, L.n_hi, cfg->n_rot, (double)cfg->rope_theta,
+                                               cfg->freq_factors, stream), "rope tables launch")))
+    return st;
+  if ((st = hip_status(mark(3, stream), "stage event"))) return st;
+
+  dca::DecodeArgs da{};
+  dca::AttnArgs& a = da.base;
+  for (int r = 0; r < 3; ++r) a.q_rot[r] = (const char*)qrot + (size_t)r * rows * Hq * R * 2;
+  a.q_rot_hs = R;
+  a.q_tail = (const char*)q + R * 2;
+  a.q_tail_hs = D;
+  a.k_raw = k_codes;
+  a.bounds = bounds;
+  a.B = B; a.T = T; a.Hq = cfg->n_head_q; a.Hkv = cfg->n_head_kv; a.n_kv = n_kv;
+  a.D = cfg->head_dim; a.n_rot = cfg->n_rot; a.scale = cfg->scale;
+  a.rot_f16 = 1;
+  da.k_scales = k_scales;
+  da.o_part = (float*)(ws + L.dec_o);
+  da.lse_part = (float*)(ws + L.dec_lse);
+  da.span = L.span;
+  da.n_spans = L.n_spans;
+  da.regime_mask = 7;
+  for (int r = 0; r < 3; ++r) da.slot0[r] = r * L.n_spans;
+  da.rot_lo = lo;
+  da.rot_hi = hi;
+  da.chunk = cfg->chunk;
+  if ((st = hip_status(dca::launch_attn_decode_q8(da, stream), "q8 decode attention launch")))
+    return st;
+  if ((st = hip_status(mark(4, stream), "stage event"))) return st;
+  dca::MergeArgs m{};
+  m.o_base = da.o_part;
+  m.lse_base = da.lse_part;
+  m.o_part_stride = rows * Hq * D;
+  m.lse_part_stride = rows * Hq;
+  m.n_parts = 3 * L.n_spans;
+  m.strided = 1;
+  m.rows = rows * Hq;
+  m.D = cfg->head_dim;
+  m.o_out = o;
+  m.lse_out = lse;
+  if ((st = hip_status(dca::launch_merge_many(m, o_dtype == DCA_BF16, stream), "split merge launch")))
+    return st;
   return hip_status(mark(5, stream), "stage event");
 }
 

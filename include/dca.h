@@ -168,6 +168,28 @@ dca_status dca_attention(const dca_config* cfg, dca_dtype dtype, int32_t B, int3
 size_t dca_attention_workspace_size(const dca_config* cfg, dca_dtype dtype, int32_t B, int32_t T,
                                     int32_t n_kv);
 
+/* dca_attention over a key cache stored as q8_0 blocks (the pages run DCA over q8_0 caches and
+ * read the codes inside the attention kernel: Upstream Sync entries "DCA all-KV" and
+ * "0119-p0-dcaon-scalar-inregister"; they give the size as about 0.53x of f16 but print no
+ * layout).  Every 32 consecutive dims of one (key, KV head) row share an fp16 scale d; the key's
+ * value in a dim is d * q with q the dim's int8 code; the values are also the values of the
+ * attention (K = V).
+ * q       : bf16 [B,T,Hq,D] pre-RoPE queries (|q| below 65504: the products run in fp16);
+ *           q_pos: int32 [B,T].
+ * k_codes : int8 [B,n_kv,Hkv,D], the codes in the key layout.
+ * k_scales: fp16 bit patterns [B,n_kv,Hkv,D/32], the scale of each block in the same order.
+ * out     : o [B,T,Hq,D] of o_dtype; lse fp32 [B,T,Hq] (may be NULL).
+ * The split-KV kernel serves every T (it is meant for decode: a few query tokens per sequence);
+ * B*T*n_head_kv must not exceed 65535.  head_dim 512, n_rot 128, n_head_q/n_head_kv in
+ * {1,2,4,8,16}, as for bf16.  The dtype of q is bf16; the stage-event hook records as for a
+ * bf16 decode.  Errors as dca_attention.
+ * workspace: at least dca_attention_q8_workspace_size() bytes of device memory. */
+dca_status dca_attention_q8(const dca_config* cfg, int32_t B, int32_t T, const void* q,
+                            const int32_t* q_pos, const int8_t* k_codes, const uint16_t* k_scales,
+                            int32_t n_kv, dca_dtype o_dtype, void* o, float* lse, void* workspace,
+                            size_t ws_bytes, hipStream_t stream);
+size_t dca_attention_q8_workspace_size(const dca_config* cfg, int32_t B, int32_t T, int32_t n_kv);
+
 /* Optional stage timing for dca_attention (measurement hook; no page defines it).  After
  * dca_set_stage_events(ev, n) with n >= DCA_N_STAGE_EVENTS, every dca_attention call made later on
  * this thread records, on its stream: ev[0] before the remap, ev[1] after the remap, ev[2] after

@@ -47,6 +47,15 @@ def _lib():
             i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_double, ctypes.c_double, f64p, ctypes.c_int,
             ctypes.c_int, i64, i64, ctypes.c_void_p, i32p, ctypes.c_void_p, i64, i64,
             ctypes.POINTER(ctypes.c_int64), f64p, f64p, f64p, f64p, ctypes.c_int]
+        lib.dca_oracle_attention_q8.restype = ctypes.c_int
+        lib.dca_oracle_attention_q8.argtypes = [
+            i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_double, ctypes.c_double, f64p, ctypes.c_int,
+            i64, i64, ctypes.c_void_p, i32p, ctypes.c_void_p, ctypes.c_void_p, i64, i64,
+            ctypes.POINTER(ctypes.c_int64), f64p, f64p, f64p, f64p, ctypes.c_int]
+        lib.dca_oracle_half.restype = ctypes.c_double
+        lib.dca_oracle_half.argtypes = [ctypes.c_uint16]
+        lib.dca_oracle_dequant_q8.restype = None
+        lib.dca_oracle_dequant_q8.argtypes = [ctypes.c_void_p, ctypes.c_void_p, i64, f64p]
         _LIB = lib
     return _LIB
 
@@ -151,6 +160,61 @@ def attention(q, qpos, k, *, chunk, n_rot, theta, scale, freq_factors=None, rows
         q.ctypes.data_as(ctypes.c_void_p), _ptr(qpos, ctypes.c_int32),
         k.ctypes.data_as(ctypes.c_void_p), N, n, _ptr(sel, ctypes.c_int64),
         _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double),
+        None if o_reg is None else _ptr(o_reg, ctypes.c_double),
+        None if lse_reg is None else _ptr(lse_reg, ctypes.c_double), int(n_threads))
+    if st != 0:
+        raise RuntimeError(f"oracle attention failed with status {st}")
+    return dict(o=o, lse=lse, o_reg=o_reg, lse_reg=lse_reg, rows=sel)
+
+
+def half(bits):
+    """Value of IEEE binary16 bit patterns (the q8_0 block scale), by the format's definition."""
+    return _lib().dca_oracle_half(int(bits) & 0xFFFF)
+
+
+def dequant_q8(codes, scales):
+    """Values d * q of a q8_0 cache (reading in the header of dca_oracle.c): codes int8 [..., D],
+    scales uint16 fp16 bits [..., D/32] -> float64 [..., D]."""
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    assert codes.shape[:-1] == scales.shape[:-1] and codes.shape[-1] == 32 * scales.shape[-1]
+    out = np.empty(codes.shape, np.float64)
+    _lib().dca_oracle_dequant_q8(codes.ctypes.data_as(ctypes.c_void_p), scales.ctypes.data_as(ctypes.c_void_p),
+                                 codes.size, _ptr(out, ctypes.c_double))
+    return out
+
+
+def attention_q8(q, qpos, codes, scales, *, chunk, n_rot, theta, scale, freq_factors=None, rows=None,
+                 per_regime=True, n_threads=0, remap_mode=REMAP_BASELINE):
+    """DCA attention (as `attention`) over a q8_0 key cache: codes int8 [B, N, Hkv, D], scales
+    uint16 fp16 bits [B, N, Hkv, D/32]; the keys (and values, K = V) are d * q.  q is float32 or
+    uint16 bf16 bits [B, T, Hq, D]."""
+    q = np.ascontiguousarray(q)
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    if q.dtype == np.uint16:
+        q_bf16 = 1
+    elif q.dtype == np.float32:
+        q_bf16 = 0
+    else:
+        raise TypeError("q must be float32 or uint16 (bf16 bits)")
+    B, T, Hq, D = q.shape
+    Bk, N, Hkv, Dk = codes.shape
+    assert Bk == B and Dk == D and scales.shape == (B, N, Hkv, D // 32)
+    qpos = np.ascontiguousarray(np.asarray(qpos, dtype=np.int32).reshape(B, T))
+    sel = np.arange(B * T, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    n = sel.size
+    o = np.zeros((n, Hq, D), np.float64)
+    lse = np.zeros((n, Hq), np.float64)
+    o_reg = np.zeros((3, n, Hq, D), np.float64) if per_regime else None
+    lse_reg = np.zeros((3, n, Hq), np.float64) if per_regime else None
+    ff = None if freq_factors is None else np.ascontiguousarray(freq_factors, dtype=np.float64)
+    st = _lib().dca_oracle_attention_q8(
+        D, int(n_rot), Hq, Hkv, int(chunk), int(remap_mode), float(theta), float(scale),
+        None if ff is None else _ptr(ff, ctypes.c_double), q_bf16, B, T,
+        q.ctypes.data_as(ctypes.c_void_p), _ptr(qpos, ctypes.c_int32),
+        codes.ctypes.data_as(ctypes.c_void_p), scales.ctypes.data_as(ctypes.c_void_p), N, n,
+        _ptr(sel, ctypes.c_int64), _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double),
         None if o_reg is None else _ptr(o_reg, ctypes.c_double),
         None if lse_reg is None else _ptr(lse_reg, ctypes.c_double), int(n_threads))
     if st != 0:

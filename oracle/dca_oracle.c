@@ -47,6 +47,15 @@
  *   y_f = x_f cos a - x_{f+n_rot/2} sin a;  y_{f+n_rot/2} = x_f sin a + x_{f+n_rot/2} cos a.
  *   Dims >= n_rot are copied.  Everything is fp64.
  *
+ * Quantized keys (q8_0): the pages run DCA over caches of type q8_0 ([U] entries "DCA all-KV"
+ * and "0119-p0-dcaon-scalar-inregister", which read the codes in registers inside the kernel) and
+ * give its size as about 0.53x of f16, but print no layout.  Reading: every 32 consecutive dims of
+ * one (key, KV head) row form a block with one fp16 scale d and 32 signed 8-bit codes q, and the
+ * key's value in a dim is d * q (34 bytes per 32 values).  The codes are stored as int8 [..][D]
+ * in the key layout and the scales as fp16 [..][D/32] in the same order.  The oracle reads the
+ * value d * q exactly (fp16 -> double by the IEEE binary16 definition) and then runs the same
+ * attention on it.
+ *
  * Scores s_j = scale * <rot(q, P_reg(j)), rot(k_j, j mod c)>, softmax over the union of the
  * regimes, O = sum_j softmax_j * k_j (un-rotated), LSE = m + ln sum_j e^(s_j - m).
  * Query head h uses KV head h / (Hq / Hkv).
@@ -179,6 +188,39 @@ static double load_in(const void* p, int64_t e, int in_bf16) {
   return (double)((const float*)p)[e];
 }
 
+/* Value of IEEE binary16 bits: sign, 5-bit exponent (bias 15), 10-bit fraction; exponent 0 is the
+ * subnormal range fraction * 2^-24, exponent 31 infinity or NaN. */
+double dca_oracle_half(uint16_t h) {
+  const int sign = h >> 15, ex = (h >> 10) & 31, fr = h & 1023;
+  double v;
+  if (ex == 0)
+    v = ldexp((double)fr, -24);
+  else if (ex == 31)
+    v = fr ? NAN : INFINITY;
+  else
+    v = ldexp((double)(1024 + fr), ex - 25);
+  return sign ? -v : v;
+}
+
+/* A key cache: fp32 (kind 0), bf16 bit patterns (kind 1) or q8_0 (kind 2: int8 codes in p, fp16
+ * scale bits in scales, one per 32 consecutive elements of a row). */
+typedef struct {
+  const void* p;
+  const uint16_t* scales;
+  int kind;
+} kv_src;
+
+static double load_k(const kv_src* k, int64_t e) {
+  if (k->kind == 2) return dca_oracle_half(k->scales[e / 32]) * (double)((const int8_t*)k->p)[e];
+  return load_in(k->p, e, k->kind);
+}
+
+/* Dequantized values of n elements of a q8_0 cache (codes + fp16 scales), for the tests. */
+void dca_oracle_dequant_q8(const int8_t* codes, const uint16_t* scales, int64_t n, double* out) {
+  kv_src k = {codes, scales, 2};
+  for (int64_t e = 0; e < n; ++e) out[e] = load_k(&k, e);
+}
+
 /* Round-to-nearest-even of a double to bf16 (through fp32, as a rotated value is formed in fp32
  * and then stored as bf16), returned as a double. */
 static double round_bf16(double v) {
@@ -223,14 +265,14 @@ void dca_oracle_merge(int64_t n_parts, const double* o_parts, const double* lse_
  * the scores are formed: the contract of a caller that hands over bf16 rotated operands (used to
  * check the per-regime entry point); 0 keeps them exact.
  * Returns 0, or -1 on allocation failure, -2 on a bad argument. */
-int dca_oracle_attention(int64_t D, int64_t n_rot, int64_t Hq, int64_t Hkv, int64_t c, int mode,
-                         double theta, double scale, const double* ff, int in_bf16, int rot_round,
-                         int64_t B,
-                         int64_t T, const void* q, const int32_t* qpos, const void* k, int64_t n_kv,
-                         int64_t n_sel, const int64_t* sel, double* o, double* lse, double* o_reg,
-                         double* lse_reg, int n_threads) {
+static int attention_impl(int64_t D, int64_t n_rot, int64_t Hq, int64_t Hkv, int64_t c, int mode,
+                          double theta, double scale, const double* ff, int in_bf16, int rot_round,
+                          int64_t B, int64_t T, const void* q, const int32_t* qpos, const kv_src* kv,
+                          int64_t n_kv, int64_t n_sel, const int64_t* sel, double* o, double* lse,
+                          double* o_reg, double* lse_reg, int n_threads) {
   if (D <= 0 || n_rot <= 0 || n_rot > D || n_rot > 1024 || (n_rot & 1) || Hq <= 0 || Hkv <= 0 ||
-      Hq % Hkv || c <= 0 || mode < 0 || mode > 2 || B <= 0 || T <= 0 || n_kv < 0)
+      Hq % Hkv || c <= 0 || mode < 0 || mode > 2 || B <= 0 || T <= 0 || n_kv < 0 ||
+      (kv->kind == 2 && (D % 32 || !kv->scales)))
     return -2;
 #ifdef _OPENMP
   if (n_threads > 0) omp_set_num_threads(n_threads);
@@ -253,7 +295,7 @@ int dca_oracle_attention(int64_t D, int64_t n_rot, int64_t Hq, int64_t Hkv, int6
       double xin[1024], xout[1024];
       for (int64_t g = 0; g < Hkv; ++g) {
         for (int64_t d = 0; d < n_rot; ++d)
-          xin[d] = load_in(k, ((b * n_kv + j) * Hkv + g) * D + d, in_bf16);
+          xin[d] = load_k(kv, ((b * n_kv + j) * Hkv + g) * D + d);
         rope_one(n_rot, n_rot, theta, ff, xin, (double)dca_oracle_key_pos(j, c), xout);
         if (rot_round == 1)
           for (int64_t d = 0; d < n_rot; ++d) xout[d] = round_bf16(xout[d]);
@@ -294,7 +336,7 @@ int dca_oracle_attention(int64_t D, int64_t n_rot, int64_t Hq, int64_t Hkv, int6
             double dot = 0.0;
             for (int64_t d = 0; d < n_rot; ++d) dot += qq[d] * krot[(j * Hkv + g) * n_rot + d];
             for (int64_t d = n_rot; d < D; ++d)
-              dot += qq[d] * load_in(k, ((b * n_kv + j) * Hkv + g) * D + d, in_bf16);
+              dot += qq[d] * load_k(kv, ((b * n_kv + j) * Hkv + g) * D + d);
             s_buf[j] = scale * dot;
           }
           /* regime set -1 = the union; then each regime alone */
@@ -324,7 +366,7 @@ int dca_oracle_attention(int64_t D, int64_t n_rot, int64_t Hq, int64_t Hkv, int6
               double e = exp(s_buf[j] - m);
               Z += e;
               for (int64_t d = 0; d < D; ++d)
-                acc[d] += e * load_in(k, ((b * n_kv + j) * Hkv + g) * D + d, in_bf16);
+                acc[d] += e * load_k(kv, ((b * n_kv + j) * Hkv + g) * D + d);
             }
             for (int64_t d = 0; d < D; ++d) out_o[d] = acc[d] / Z;
             *out_l = m + log(Z);
@@ -341,4 +383,27 @@ int dca_oracle_attention(int64_t D, int64_t n_rot, int64_t Hq, int64_t Hkv, int6
     if (status) return status;
   }
   return status;
+}
+
+int dca_oracle_attention(int64_t D, int64_t n_rot, int64_t Hq, int64_t Hkv, int64_t c, int mode,
+                         double theta, double scale, const double* ff, int in_bf16, int rot_round,
+                         int64_t B,
+                         int64_t T, const void* q, const int32_t* qpos, const void* k, int64_t n_kv,
+                         int64_t n_sel, const int64_t* sel, double* o, double* lse, double* o_reg,
+                         double* lse_reg, int n_threads) {
+  kv_src kv = {k, NULL, in_bf16};
+  return attention_impl(D, n_rot, Hq, Hkv, c, mode, theta, scale, ff, in_bf16, rot_round, B, T, q,
+                        qpos, &kv, n_kv, n_sel, sel, o, lse, o_reg, lse_reg, n_threads);
+}
+
+/* The same attention over a q8_0 key cache (codes int8 [B][n_kv][Hkv][D], scales fp16 bits
+ * [B][n_kv][Hkv][D/32]); queries fp32 (q_bf16 = 0) or bf16 bit patterns (q_bf16 = 1). */
+int dca_oracle_attention_q8(int64_t D, int64_t n_rot, int64_t Hq, int64_t Hkv, int64_t c, int mode,
+                            double theta, double scale, const double* ff, int q_bf16, int64_t B,
+                            int64_t T, const void* q, const int32_t* qpos, const int8_t* codes,
+                            const uint16_t* scales, int64_t n_kv, int64_t n_sel, const int64_t* sel,
+                            double* o, double* lse, double* o_reg, double* lse_reg, int n_threads) {
+  kv_src kv = {codes, scales, 2};
+  return attention_impl(D, n_rot, Hq, Hkv, c, mode, theta, scale, ff, q_bf16, 0, B, T, q, qpos,
+                        &kv, n_kv, n_sel, sel, o, lse, o_reg, lse_reg, n_threads);
 }

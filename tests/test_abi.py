@@ -93,3 +93,29 @@ def test_other_validation_paths():
     # empty work is a no-op that succeeds
     assert L.dca_attention(ctypes.byref(c), dca.BF16, 0, 4, None, None, None, 4, dca.BF16, None,
                            None, None, 0, None) == dca.OK
+
+
+def test_q8_entry_point_validation():
+    if not os.path.exists(dca.LIB_PATH):
+        pytest.skip("libdca.so not built")
+    L = dca.lib()
+    c = _cfg()
+    vp = ctypes.c_void_p(16)
+    need = L.dca_attention_q8_workspace_size(ctypes.byref(c), 8, 1, 262144)
+    # split-KV partials for every T: 3 regimes x 64 spans of 4096 keys x 128 (row, head) x 512 fp32
+    assert need >= 3 * 64 * 128 * 512 * 4
+    assert L.dca_attention_q8(ctypes.byref(c), 8, 1, vp, vp, vp, vp, 262144, dca.BF16, vp, None, vp,
+                              need - 1, None) == dca.ERR_WORKSPACE_TOO_SMALL
+    assert L.dca_attention_q8(ctypes.byref(c), 8, 1, vp, vp, vp, None, 262144, dca.BF16, vp, None, vp,
+                              need, None) == dca.ERR_INVALID_ARGUMENT     # scales missing
+    assert L.dca_attention_q8(ctypes.byref(c), 8, 1, vp, vp, vp, vp, 262144, 7, vp, None, vp,
+                              need, None) == dca.ERR_INVALID_ARGUMENT     # bad output dtype
+    bad = _cfg(head_dim=256)
+    assert L.dca_attention_q8(ctypes.byref(bad), 8, 1, vp, vp, vp, vp, 4, dca.BF16, vp, None, vp,
+                              1 << 30, None) == dca.ERR_UNSUPPORTED
+    assert L.dca_attention_q8_workspace_size(ctypes.byref(bad), 8, 1, 4) == 0
+    # more (row, KV head) pairs than the split-KV grid takes
+    assert L.dca_attention_q8(ctypes.byref(c), 40000, 1, vp, vp, vp, vp, 4, dca.BF16, vp, None, vp,
+                              1 << 40, None) == dca.ERR_UNSUPPORTED
+    assert L.dca_attention_q8(ctypes.byref(c), 0, 1, None, None, None, None, 4, dca.BF16, None, None,
+                              None, 0, None) == dca.OK

@@ -437,3 +437,93 @@ def test_bf16_rounding_matches_torch():
     ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(ours, ref)
     assert np.array_equal(synth.bf16_to_f32(ours), torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+# ----------------------------------------------------------------------------------------------
+# q8_0 key cache
+# ----------------------------------------------------------------------------------------------
+
+def test_half_matches_numpy_float16_on_every_bit_pattern():
+    """The oracle's binary16 decoder against numpy's float16 on all 65536 patterns."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    want = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.half(int(b)) for b in bits])
+    nan = np.isnan(want)
+    assert (np.isnan(got) == nan).all()
+    assert np.array_equal(got[~nan], want[~nan])
+    # hand values: 1, the smallest subnormal, -2, the largest finite, -0
+    assert [oracle.half(b) for b in (0x3C00, 0x0001, 0xC000, 0x7BFF)] == [1.0, 2.0 ** -24, -2.0, 65504.0]
+    assert math.copysign(1.0, oracle.half(0x8000)) == -1.0
+
+
+def test_dequant_q8_hand_example():
+    """Two blocks of one row, worked by hand: block 0 has d = 0.5 (0x3800), block 1 d = -3 * 2^-24
+    (a negative subnormal scale, 0x8003); each value is d times its code."""
+    codes = np.zeros((1, 64), np.int8)
+    codes[0, :6] = [-128, -1, 0, 1, 127, 5]
+    codes[0, 32:35] = [3, -7, 100]
+    codes[0, 63] = -2
+    scales = np.array([[0x3800, 0x8003]], np.uint16)
+    want = np.zeros((1, 64))
+    want[0, :6] = [-64.0, -0.5, 0.0, 0.5, 63.5, 2.5]
+    s1 = -3.0 * 2.0 ** -24
+    want[0, 32:35] = [3 * s1, -7 * s1, 100 * s1]
+    want[0, 63] = -2 * s1
+    got = oracle.dequant_q8(codes, scales)
+    assert np.array_equal(got, want)
+
+
+def test_q8_quantizer_round_trip_bound():
+    """The synthetic q8_0 store: codes in [-127, 127], every nonzero block reaches |code| = 127,
+    and d*q is within d/2 (half a step) plus the fp16 rounding of d of the drawn value."""
+    x = np.random.default_rng(12).standard_normal((50, 3, 96)).astype(np.float32) * 4
+    x[0, 0, :32] = 0.0                       # an all-zero block
+    x[1, 1, 32:64] = 1e-6                    # a constant block of a tiny value (subnormal scale)
+    codes, scales = synth.q8_0_blocks(x)
+    assert codes.shape == x.shape and scales.shape == (50, 3, 3)
+    assert codes.min() >= -127 and codes.max() <= 127
+    blk = np.abs(codes.reshape(50, 3, 3, 32)).max(axis=-1)
+    nonzero = np.abs(x.reshape(50, 3, 3, 32)).max(axis=-1) > 0
+    assert (blk[nonzero] == 127).all() and (blk[~nonzero] == 0).all()
+    d_exact = np.abs(x.reshape(50, 3, 3, 32)).max(axis=-1).astype(np.float64) / 127
+    deq = oracle.dequant_q8(codes, scales).reshape(50, 3, 3, 32)
+    err = np.abs(deq - x.reshape(50, 3, 3, 32).astype(np.float64))
+    d_store = scales.view(np.float16).astype(np.float64)
+    bound = d_exact / 2 * (1 + 1e-6) + np.abs(d_store - d_exact) * 127 + 1e-30
+    assert (err <= bound[..., None]).all()
+
+
+def test_q8_generator_is_deterministic_and_blocks_agree():
+    """The chunked, threaded store equals q8_0_blocks of the same draws, for any chunking."""
+    shape = (2, 40, 2, 64)
+    c1, s1 = synth._normal_q8(np.random.default_rng(4), shape, chunk_elems=1 << 10)
+    c2, s2 = synth._normal_q8(np.random.default_rng(4), shape, chunk_elems=1 << 14)
+    x = np.random.default_rng(4).standard_normal(int(np.prod(shape)), dtype=np.float32).reshape(shape)
+    c3, s3 = synth.q8_0_blocks(x)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+    assert np.array_equal(c1, c3) and np.array_equal(s1, s3)
+
+
+@pytest.mark.parametrize("mode", [oracle.REMAP_BASELINE, oracle.REMAP_PAGE_C])
+def test_attention_q8_equals_attention_over_the_dequantized_cache(mode):
+    """A q8_0 value d*q (11-bit times 8-bit significand) is exact in float32, so attention over the
+    q8_0 cache must equal, to the last bit, attention over the float32 cache of d*q with the bf16
+    queries widened to float32."""
+    w = synth.Workload("t8", 2, 9, 40, 49, 8, 4, 2, "q8_0", 21, D=64, n_rot=16)
+    inp = synth.make_inputs(w)
+    ff = inp["freq_factors"].astype(np.float64)
+    kw = dict(chunk=w.chunk, n_rot=w.n_rot, theta=w.theta, scale=0.125, freq_factors=ff, remap_mode=mode)
+    res = oracle.attention_q8(inp["q"], inp["q_pos"], inp["k_codes"], inp["k_scales"], **kw)
+    kf = oracle.dequant_q8(inp["k_codes"], inp["k_scales"])
+    assert np.array_equal(kf.astype(np.float32).astype(np.float64), kf)
+    ref = oracle.attention(synth.bf16_to_f32(inp["q"]), inp["q_pos"], kf.astype(np.float32), **kw)
+    for key in ("o", "lse", "o_reg", "lse_reg"):
+        assert np.array_equal(res[key], ref[key]), key
+    # the cache really is quantized: the unquantized draws (the stream after Q) give a nearby but
+    # different answer
+    rng = np.random.default_rng(w.seed)
+    synth._normal(rng, inp["q"].shape, True)
+    kx = rng.standard_normal(kf.size, dtype=np.float32).reshape(kf.shape)
+    assert np.abs(kf - kx).max() <= np.abs(kx).max() / 127 / 2 * 1.01
+    raw = oracle.attention(synth.bf16_to_f32(inp["q"]), inp["q_pos"], kx, **kw)
+    assert 0 < np.abs(raw["lse"] - res["lse"]).max() < 0.05
