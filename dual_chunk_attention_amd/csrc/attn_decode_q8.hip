@@ -8,11 +8,15 @@
 // 544 bytes per key and head instead of 1024:
 //  * Each workgroup (4 waves) handles one (query row, KV head, span of keys) as in the bf16
 //    passes.  64-key tiles of codes (32 KiB) and scales (2 KiB) come in by direct global->LDS
-//    loads, double buffered.
-//  * Wave w turns the codes of keys [16w, 16w+16) into fp16 values d*q (one rounding) in a 64 KiB
-//    fp16 tile laid out like the bf16 passes' tile; from there the score and value operands are
-//    read exactly as in those passes, and both products run as fp16 MFMA 16x16x32 (the query's
+//    loads, double buffered; at ~78 KiB of LDS two workgroups share a CU.
+//  * No dequantized copy of the tile is stored.  The score operand (key rows, 8 dims per lane) is
+//    read as codes and turned into fp16 d*q in registers; the value operand (8 keys of one dim per
+//    lane) is read with gfx950's 8-bit transposing LDS read and scaled per key from a small
+//    transposed copy of the tile's scales.  Both products run as fp16 MFMA 16x16x32 (the query's
 //    raw dims are converted from bf16 to fp16 once per row, the probabilities are fp16).
+//  * Code rows sit in LDS with their 16-byte chunks XOR-swizzled by the row's low 4 bits (the
+//    loads pick the global chunk that belongs at each position), so that both the 16-row score
+//    reads and the 8-row transposing reads hit 16 distinct chunk slots.
 //  * The rotary dims of a key are rotated in registers at j mod c from the fp64-built cos/sin
 //    tables (lo[p & 63] composed with hi[p >> 6]), as in the bf16 passes.
 //  * Codes to fp16: with u = q + 128 (the byte xor 0x80), the fp16 bit pattern 0x6400 | u is
@@ -24,29 +28,38 @@ namespace {
 
 constexpr int kD = 512;
 constexpr int kTile = 64;
-constexpr int kCodeBytes = kTile * kD;          // 32 KiB of int8 codes per tile
-constexpr int kScaleBytes = kTile * kD / 32 * 2;  // 2 KiB of fp16 scales per tile
-constexpr int kStageBytes = kCodeBytes + kScaleBytes;
-constexpr int kF16Bytes = kTile * kD * 2;       // 64 KiB fp16 tile
+constexpr int kCodeBytes = kTile * kD;            // 32 KiB of int8 codes per tile
+constexpr int kScaleBytes = kTile * kD / 32 * 2;  // 2 KiB of fp16 scales per tile, [key][block]
+constexpr int kHiRow = kCodeBytes + kScaleBytes;  // hi table row of the tile
+constexpr int kStageBytes = kHiRow + 512;
 constexpr float kTau = 8.0f;
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i lds_v2i;
 
-// 16-byte chunk swizzle of an fp16 tile row (conflict-free 16-row b128 reads and 4-row transpose
-// reads on gfx950's 256-byte bank window), the same as the bf16 passes' tile.
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+// a value the compiler cannot see through, so that lane-dependent address arithmetic is redone in
+// the tile loop instead of being hoisted out of it into long-lived registers
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
-// eight int8 codes (two words) times the fp16 scale d -> eight fp16 values d*q
-__device__ __forceinline__ f16x8 dequant8(uint32_t lo, uint32_t hi, _Float16 d) {
+// eight int8 codes (two words, byte i = element i) -> fp16 (1024 + u) bit patterns, u = code + 128
+__device__ __forceinline__ void biased8(uint32_t lo, uint32_t hi, f16x2 h[4]) {
   const uint32_t ul = lo ^ 0x80808080u, uh = hi ^ 0x80808080u;
-  const f16x2 dd = {d, d};
-  const f16x2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
-  f16x2 h[4];
   h[0] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, ul, 0x04010400u));
   h[1] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, ul, 0x04030402u));
   h[2] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, uh, 0x04010400u));
   h[3] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, uh, 0x04030402u));
+}
+
+// eight codes of one block times its scale d -> eight fp16 values d*q
+__device__ __forceinline__ f16x8 dequant8(uint32_t lo, uint32_t hi, _Float16 d) {
+  f16x2 h[4];
+  biased8(lo, hi, h);
+  const f16x2 dd = {d, d};
+  const f16x2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
   f16x8 out;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -57,18 +70,32 @@ __device__ __forceinline__ f16x8 dequant8(uint32_t lo, uint32_t hi, _Float16 d) 
   return out;
 }
 
-__global__ __launch_bounds__(256, 1) void attn_decode_q8_kernel(DecodeArgs da) {
+// eight codes of one dim over eight keys, each with its own scale (dd[i] = scales of keys 2i, 2i+1)
+__device__ __forceinline__ f16x8 dequant8_keys(uint32_t lo, uint32_t hi, const f16x2 dd[4]) {
+  f16x2 h[4];
+  biased8(lo, hi, h);
+  const f16x2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
+  f16x8 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16x2 v = (h[i] - off) * dd[i];
+    out[2 * i] = v[0];
+    out[2 * i + 1] = v[1];
+  }
+  return out;
+}
+
+__global__ __launch_bounds__(256, 2) void attn_decode_q8_kernel(DecodeArgs da) {
   const AttnArgs& a = da.base;
   __shared__ __attribute__((aligned(1024))) char stage[2 * kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char kbuf[kF16Bytes];
   __shared__ __attribute__((aligned(16))) _Float16 pbuf[16 * kTile];   // P[head][key]
-  __shared__ __attribute__((aligned(1024))) float2 hbuf[2][128];         // hi table row of a tile
+  __shared__ __attribute__((aligned(16))) _Float16 sT[16 * kTile];     // tile scales, [block][key]
+  __shared__ __attribute__((aligned(16))) char qsm[16 * 256];          // rotated query dims, fp16
   __shared__ float smax[4][16], ssum[4][16], wsum[4][16];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const uint32_t stage_lds = (uint32_t)(uintptr_t)(lds_char*)stage;
-  const uint32_t hbuf_lds = (uint32_t)(uintptr_t)(lds_char*)&hbuf[0][0];
   const int hcol = l & 15, gq = l >> 4;   // column (query head) and 16-lane group
   const int G = a.Hq / a.Hkv;
   const int64_t rows = (int64_t)a.B * a.T;
@@ -88,7 +115,8 @@ __global__ __launch_bounds__(256, 1) void attn_decode_q8_kernel(DecodeArgs da) {
   const float scale_log2 = a.scale * kLog2e;
 
   // query fragments (fp16): B operand lane l holds Q[head hcol][32 s + 8 gq .. +7]; the raw dims
-  // come in as bf16 and are converted once
+  // come in as bf16 and are converted once into registers, the rotated dims (s < 4, one set per
+  // regime) are read per tile from LDS (head h's 16-byte chunk c at position c ^ h)
   f16x8 q[16];
   {
     const bf16* qt = (const bf16*)a.q_tail + rowhead * a.q_tail_hs + 8 * gq;
@@ -101,17 +129,11 @@ __global__ __launch_bounds__(256, 1) void attn_decode_q8_kernel(DecodeArgs da) {
       q[s] = h;
     }
   }
-  // LDS offsets.  QK operand: key row 16w + hcol, chunk 4s + gq.
-  const int qrow = 16 * w + hcol;
-  int qk_off[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) qk_off[u] = qrow * 1024 + 16 * ((4 * u + gq) ^ swz(qrow));
-  const int j16 = l & 15;
+  const int qrow = 16 * w + hcol;   // the lane's key row in the score product
 
   // Key rotation from the tables (see the bf16 passes): with c a multiple of 64 the lane's lo
   // entries stay in registers and the tile's hi row travels to LDS with the tile's loads.
   const bool tab_tile = da.chunk % 64 == 0;
-  const int n_hi = (da.chunk + 63) / 64;
   float2 lo_q[16];
   if (tab_tile) {
 #pragma unroll
@@ -132,12 +154,12 @@ __global__ __launch_bounds__(256, 1) void attn_decode_q8_kernel(DecodeArgs da) {
       continue;
     }
     {
-      const bf16* qr = (const bf16*)a.q_rot[r] + rowhead * a.q_rot_hs + 8 * gq;   // fp16 bits
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 v = *(const bf16x8*)(qr + 32 * s);
-        q[s] = head_ok ? __builtin_bit_cast(f16x8, v) : f16x8{};
-      }
+      // thread t: head t >> 4, dims 8 (t & 15) .. +7 (fp16 bits)
+      const int h = tid >> 4, c = tid & 15;
+      bf16x8 v{};
+      if (h < G)
+        v = *(const bf16x8*)((const bf16*)a.q_rot[r] + (bt * a.Hq + (int64_t)g * G + h) * a.q_rot_hs + 8 * c);
+      *(bf16x8*)(qsm + h * 256 + 16 * (c ^ h)) = v;
     }
     f32x4 o[8];
 #pragma unroll
@@ -147,85 +169,114 @@ __global__ __launch_bounds__(256, 1) void attn_decode_q8_kernel(DecodeArgs da) {
     float m_used = -INFINITY, l_part = 0.0f, w_part = 0.0f;
 
     const int kt0 = lo / kTile, kt1 = hi / kTile;
-    // tile k0..k0+63 by direct global->LDS loads into stage buf: wave w the code rows 16w..16w+15
-    // (two 512-byte rows per load), waves 0 and 1 the scale rows 0..31 and 32..63 (lane l the
-    // half l%2 of row l/2); rows past the cache re-read its last key (their scores are masked)
+    // tile k0..k0+63 by direct global->LDS loads into stage buf: wave w the code rows
+    // 16w..16w+15 (two 512-byte rows per load; position p of row r receives global chunk
+    // p ^ (r & 15)), waves 0 and 1 the scale rows 0..31 and 32..63 (lane l the half l%2 of row
+    // l/2), lanes 0..31 of wave 2 the hi table row; rows past the cache re-read its last key
+    // (their scores are masked)
     auto issue = [&](int buf, int k0) {
       const uint32_t base = stage_lds + buf * kStageBytes;
+      const int ln = opaque(l);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int row = 16 * wu + 2 * i + (l >> 5);
+        const int row = 16 * wu + 2 * i + (ln >> 5);
         const int key = min(max(k0 + row, 0), a.n_kv - 1);
-        dma16(codes_b + (int64_t)key * a.Hkv * kD + 16 * (l & 31), base + (16 * wu + 2 * i) * 512);
+        dma16(codes_b + (int64_t)key * a.Hkv * kD + 16 * ((ln & 31) ^ (row & 15)),
+              base + (16 * wu + 2 * i) * 512);
       }
       if (wu < 2) {
-        const int row = 32 * wu + (l >> 1);
+        const int row = 32 * wu + (ln >> 1);
         const int key = min(max(k0 + row, 0), a.n_kv - 1);
-        dma16(scales_b + (int64_t)key * a.Hkv * (kD / 32) + 8 * (l & 1), base + kCodeBytes + wu * 1024);
+        dma16(scales_b + (int64_t)key * a.Hkv * (kD / 32) + 8 * (ln & 1), base + kCodeBytes + wu * 1024);
       }
-      if (tab_tile && wu == 3) {   // hi row of the tile (lanes 32..63 fetch the next row, unused)
-        const int hr = min((int)((int64_t)k0 % da.chunk >> 6) + (l >> 5), n_hi - 1);
-        dma16(da.rot_hi + (int64_t)hr * half_rot + 2 * (l & 31), hbuf_lds + buf * 1024);
+      if (tab_tile && wu == 2 && ln < 32) {   // hi row of the tile (512 bytes: lanes 0..31)
+        const int hr = (int)((int64_t)k0 % da.chunk >> 6);
+        dma16(da.rot_hi + (int64_t)hr * half_rot + 2 * ln, base + kHiRow);
       }
     };
     issue(0, kt0 * kTile);
-    wait_vm0();
-    __syncthreads();
 
     for (int kt = kt0; kt <= kt1; ++kt) {
       const int cur = (kt - kt0) & 1;
       const int k0 = kt * kTile;
+      // tile kt has landed (every wave's loads) and every wave is done with tile kt - 1
+      wait_vm0();
+      __syncthreads();
       if (kt < kt1) issue(cur ^ 1, k0 + kTile);
-      const int key = k0 + qrow;
+      const char* st = stage + cur * kStageBytes;
+      // lane-dependent offsets, recomputed per tile
+      const int ln = opaque(l);
+      const int lh = ln & 15, lg = ln >> 4;
+      const int lrow = 16 * w + lh;
+      // score operand: key row lrow (swizzle key lh), 8 dims at 32 s + 8 lg: chunk 2 s + (lg >> 1)
+      const char* kq = st + lrow * 512 + 8 * (lg & 1);
+      const int kq_x = (lg >> 1) ^ lh;
+      // value operand: transposing reads of rows 32 ks + 8 lg + (lh >> 1), bytes 8 (lh & 1) of the
+      // chunk of dims 128 w + 16 dt; swizzle key = the row's low 4 bits = 8 (lg & 1) + (lh >> 1),
+      // and with dt < 8: (8 w + dt) ^ key = ((8 w) ^ key) ^ dt
+      const int pv_row = 8 * lg + (lh >> 1);
+      const char* vrow = st + pv_row * 512 + 8 * (lh & 1);
+      const int pv_x = (8 * w) ^ (pv_row & 15);
 
-      // ---- codes of keys [16w, 16w+16) -> fp16 tile rows (lane l: dims 8l..8l+7 of a row) -----
+      // ---- scales: the lane's key row for the scores, and the transposed copy for the values
+      f16x8 dsc[2];
+      dsc[0] = *(const f16x8*)(st + kCodeBytes + lrow * 32);
+      dsc[1] = *(const f16x8*)(st + kCodeBytes + lrow * 32 + 16);
       {
-        const char* st = stage + cur * kStageBytes;
-#pragma unroll 4
-        for (int i = 0; i < 16; ++i) {
-          const int row = 16 * w + i;
-          const uint2 c8 = *(const uint2*)(st + row * 512 + 8 * l);
-          const _Float16 d = __builtin_bit_cast(_Float16, *(const uint16_t*)(st + kCodeBytes + row * 32 + 2 * (l >> 2)));
-          *(f16x8*)(kbuf + row * 1024 + 16 * (l ^ swz(row))) = dequant8(c8.x, c8.y, d);
-        }
+        const uint2 d4 = *(const uint2*)(st + kCodeBytes + lrow * 32 + 8 * lg);   // blocks 4lg..+3
+        uint16_t* t = (uint16_t*)sT + 4 * lg * kTile + lrow;
+        t[0 * kTile] = (uint16_t)d4.x;
+        t[1 * kTile] = (uint16_t)(d4.x >> 16);
+        t[2 * kTile] = (uint16_t)d4.y;
+        t[3 * kTile] = (uint16_t)(d4.y >> 16);
       }
-      const char* kb = kbuf;
 
-      // ---- S^T for keys [16w, 16w+16) (the wave's own rows: no barrier needed) ----------------
-      f16x8 kf[16];
-#pragma unroll
-      for (int s = 0; s < 16; ++s) kf[s] = *(const f16x8*)(kb + qk_off[s & 3] + 256 * (s >> 2));
+      // ---- S^T for keys [16w, 16w+16): codes -> fp16 d*q in registers ------------------------
+      auto kfrag = [&](int s) {
+        const uint2 c8 = *(const uint2*)(kq + 16 * ((2 * s) ^ kq_x));
+        return dequant8(c8.x, c8.y, dsc[s >> 3][s & 7]);
+      };
+      f32x4 sacc = f32x4{};
       {
+        f16x8 kr[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) kr[s] = kfrag(s);
         // rotate the rotary pairs (f, f + 64) of the lane's key by (cos, sin) of pos * w_f,
         // composed from the lo and hi tables by the angle-addition formulas
         auto rotate = [&](auto lo_of, auto hi_of) {
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
+            __builtin_amdgcn_sched_barrier(0);   // one half at a time: bounds the live table entries
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               const int f = 32 * s + 8 * gq + e;
               const float2 A = lo_of(8 * s + e, f), Bv = hi_of(f);
               const float cs = A.x * Bv.x - A.y * Bv.y;
               const float sn = A.y * Bv.x + A.x * Bv.y;
-              const float x0 = (float)kf[s][e], x1 = (float)kf[s + 2][e];
-              kf[s][e] = (_Float16)fmaf(x0, cs, -x1 * sn);
-              kf[s + 2][e] = (_Float16)fmaf(x0, sn, x1 * cs);
+              const float x0 = (float)kr[s][e], x1 = (float)kr[s + 2][e];
+              kr[s][e] = (_Float16)fmaf(x0, cs, -x1 * sn);
+              kr[s + 2][e] = (_Float16)fmaf(x0, sn, x1 * cs);
             }
           }
         };
         if (tab_tile) {
-          const float2* th = &hbuf[cur][0];
+          const float2* th = (const float2*)(st + kHiRow);
           rotate([&](int i, int) { return lo_q[i]; }, [&](int f) { return th[f]; });
         } else {
-          const int64_t pos = (int64_t)min(key, a.n_kv - 1) % da.chunk;
+          const int64_t pos = (int64_t)min(k0 + lrow, a.n_kv - 1) % da.chunk;
           const float2* tlo = da.rot_lo + (pos & 63) * half_rot;
           const float2* thi = da.rot_hi + (pos >> 6) * half_rot;
           rotate([&](int, int f) { return tlo[f]; }, [&](int f) { return thi[f]; });
         }
-      }
-      f32x4 sacc = f32x4{};
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int s = 0; s < 16; ++s) sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[s], q[s], sacc, 0, 0, 0);
+        for (int s = 0; s < 4; ++s) {
+          const f16x8 qs = *(const f16x8*)(qsm + lh * 256 + 16 * ((4 * s + lg) ^ lh));
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kr[s], qs, sacc, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int s = 4; s < 16; ++s) sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kfrag(s), q[s], sacc, 0, 0, 0);
       // C layout: reg e = key 16w + 4 gq + e, column = head hcol
       float sv[4];
       float mx = -INFINITY;
@@ -238,7 +289,7 @@ __global__ __launch_bounds__(256, 1) void attn_decode_q8_kernel(DecodeArgs da) {
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       if (gq == 0) smax[w][hcol] = mx;
-      __syncthreads();   // also: every wave's fp16 rows are in the tile before the PV reads
+      __syncthreads();   // also: the transposed scales are complete before the value reads
       const float tmax = fmaxf(fmaxf(smax[0][hcol], smax[1][hcol]), fmaxf(smax[2][hcol], smax[3][hcol]));
       const bool need = tmax > m_used + kTau;
       if (__ballot(need)) {
@@ -258,31 +309,28 @@ __global__ __launch_bounds__(256, 1) void attn_decode_q8_kernel(DecodeArgs da) {
         pv[e] = (_Float16)p;
         w_part += (float)pv[e];
       }
-      *(uint2*)(pbuf + hcol * kTile + 16 * w + 4 * gq) = __builtin_bit_cast(uint2, pv);
+      *(uint2*)(pbuf + lh * kTile + 16 * w + 4 * lg) = __builtin_bit_cast(uint2, pv);
       __syncthreads();
 
-      // ---- O^T += V^T P^T for dims [128w, 128w+128) --------------------------------------
+      // ---- O^T += V^T P^T for dims [128w, 128w+128) ------------------------------------------
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const f16x8 pb = *(const f16x8*)(pbuf + hcol * kTile + 32 * ks + 8 * gq);
+        const f16x8 pb = *(const f16x8*)(pbuf + lh * kTile + 32 * ks + 8 * lg);
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          bf16x4 v[2];
+        for (int bb = 0; bb < 4; ++bb) {
+          // scales of block 4w + bb for keys 32 ks + 8 gq .. +7, as pairs
+          const f16x8 d8 = *(const f16x8*)(sT + (4 * w + bb) * kTile + 32 * ks + 8 * lg);
+          const f16x2 dd[4] = {{d8[0], d8[1]}, {d8[2], d8[3]}, {d8[4], d8[5]}, {d8[6], d8[7]}};
 #pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int row = 32 * ks + 8 * gq + 4 * e + (j16 >> 2);
-            const int c = 16 * w + 2 * dt + ((j16 >> 1) & 1);
-            const int off = row * 1024 + 16 * (c ^ swz(row)) + 8 * (j16 & 1);
-            v[e] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(kb + off));
+          for (int h = 0; h < 2; ++h) {
+            const int dt = 2 * bb + h;
+            const v2i c = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (lds_v2i*)(lds_char*)(vrow + 32 * ks * 512 + 16 * (pv_x ^ dt)));
+            const f16x8 vf = dequant8_keys((uint32_t)c[0], (uint32_t)c[1], dd);
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pb, o[dt], 0, 0, 0);
           }
-          bf16x8 vf;
-          vf[0] = v[0][0]; vf[1] = v[0][1]; vf[2] = v[0][2]; vf[3] = v[0][3];
-          vf[4] = v[1][0]; vf[5] = v[1][1]; vf[6] = v[1][2]; vf[7] = v[1][3];
-          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, vf), pb, o[dt], 0, 0, 0);
         }
       }
-      wait_vm0();
-      __syncthreads();
     }
 
     // ---- combine the row sums of the 4 waves and store the partial ----------------------------
