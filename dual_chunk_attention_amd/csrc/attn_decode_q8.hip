@@ -11,16 +11,17 @@
 //    loads, double buffered; at ~78 KiB of LDS two workgroups share a CU.
 //  * No dequantized copy of the tile is stored.  The score operand (key rows, 8 dims per lane) is
 //    read as codes and turned into fp16 d*q in registers; the value operand (8 keys of one dim per
-//    lane) is read with gfx950's 8-bit transposing LDS read and scaled per key from a small
-//    transposed copy of the tile's scales.  Both products run as fp16 MFMA 16x16x32 (the query's
-//    raw dims are converted from bf16 to fp16 once per row, the probabilities are fp16).
+//    lane) is read with gfx950's 8-bit transposing LDS read as exact integer codes, and each key's
+//    block scale multiplies its probability instead (from a small transposed copy of the tile's
+//    scales).  Both products run as fp16 MFMA 16x16x32 (the query's raw dims are converted from
+//    bf16 to fp16 once per row, the probabilities are fp16).
 //  * Code rows sit in LDS with their 16-byte chunks XOR-swizzled by the row's low 4 bits (the
 //    loads pick the global chunk that belongs at each position), so that both the 16-row score
 //    reads and the 8-row transposing reads hit 16 distinct chunk slots.
 //  * The rotary dims of a key are rotated in registers at j mod c from the fp64-built cos/sin
 //    tables (lo[p & 63] composed with hi[p >> 6]), as in the bf16 passes.
-//  * Codes to fp16: with u = q + 128 (the byte xor 0x80), the fp16 bit pattern 0x6400 | u is
-//    1024 + u exactly, so (that - 1152) is q exactly and one fp16 multiply by d gives d*q.
+//  * Codes to fp16: every int8 code is an exact fp16 integer (one conversion each); one fp16
+//    multiply by d gives d*q.
 #include "common.h"
 
 namespace dca {
@@ -45,44 +46,33 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
-// eight int8 codes (two words, byte i = element i) -> fp16 (1024 + u) bit patterns, u = code + 128
-__device__ __forceinline__ void biased8(uint32_t lo, uint32_t hi, f16x2 h[4]) {
-  const uint32_t ul = lo ^ 0x80808080u, uh = hi ^ 0x80808080u;
-  h[0] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, ul, 0x04010400u));
-  h[1] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, ul, 0x04030402u));
-  h[2] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, uh, 0x04010400u));
-  h[3] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, uh, 0x04030402u));
+// eight int8 codes (two words, byte i = element i) -> the exact integers as fp16: each byte is
+// sign-extended and converted by an SDWA-form int16 -> fp16 conversion that writes one half of the
+// destination (one instruction per code)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ f16x8 codes8(uint32_t lo, uint32_t hi) {
+  uint32_t r0, r1, r2, r3;
+  asm("v_cvt_f16_i16_sdwa %0, sext(%4) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_0\n\t"
+      "v_cvt_f16_i16_sdwa %1, sext(%4) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_2\n\t"
+      "v_cvt_f16_i16_sdwa %2, sext(%5) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_0\n\t"
+      "v_cvt_f16_i16_sdwa %3, sext(%5) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_2\n\t"
+      "v_cvt_f16_i16_sdwa %0, sext(%4) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1\n\t"
+      "v_cvt_f16_i16_sdwa %1, sext(%4) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3\n\t"
+      "v_cvt_f16_i16_sdwa %2, sext(%5) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1\n\t"
+      "v_cvt_f16_i16_sdwa %3, sext(%5) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(lo), "v"(hi));
+  const uint32_t r[4] = {r0, r1, r2, r3};
+  return __builtin_bit_cast(f16x8, r);
 }
+#pragma clang diagnostic pop
 
-// eight codes of one block times its scale d -> eight fp16 values d*q
+// eight codes of one block times its scale d -> eight fp16 values d*q (one rounding)
 __device__ __forceinline__ f16x8 dequant8(uint32_t lo, uint32_t hi, _Float16 d) {
-  f16x2 h[4];
-  biased8(lo, hi, h);
-  const f16x2 dd = {d, d};
-  const f16x2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
-  f16x8 out;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const f16x2 v = (h[i] - off) * dd;
-    out[2 * i] = v[0];
-    out[2 * i + 1] = v[1];
-  }
-  return out;
-}
-
-// eight codes of one dim over eight keys, each with its own scale (dd[i] = scales of keys 2i, 2i+1)
-__device__ __forceinline__ f16x8 dequant8_keys(uint32_t lo, uint32_t hi, const f16x2 dd[4]) {
-  f16x2 h[4];
-  biased8(lo, hi, h);
-  const f16x2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
-  f16x8 out;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const f16x2 v = (h[i] - off) * dd[i];
-    out[2 * i] = v[0];
-    out[2 * i + 1] = v[1];
-  }
-  return out;
+  const f16x8 c = codes8(lo, hi);
+  const f16x8 dd = {d, d, d, d, d, d, d, d};
+  return c * dd;
 }
 
 __global__ __launch_bounds__(256, 2) void attn_decode_q8_kernel(DecodeArgs da) {
@@ -177,21 +167,34 @@ __global__ __launch_bounds__(256, 2) void attn_decode_q8_kernel(DecodeArgs da) {
     auto issue = [&](int buf, int k0) {
       const uint32_t base = stage_lds + buf * kStageBytes;
       const int ln = opaque(l);
+      const int last = a.n_kv - 1 - k0;   // the tile's last row inside the cache
+      const uint32_t key_bytes = (uint32_t)a.Hkv * kD, key_sbytes = (uint32_t)a.Hkv * (kD / 32) * 2;
+      const char* cb = uniform_ptr((const char*)codes_b + (int64_t)k0 * key_bytes);
+      // row 16 wu + 2 i + hb (hb = ln >> 5) has swizzle key 2 i + hb = 2 i ^ hb, so the lane's
+      // chunk offset is x ^ 32 i with x = 16 ((ln & 31) ^ hb)
+      const int hb = ln >> 5;
+      const uint32_t x = 16 * ((ln & 31) ^ hb);
+      if (last >= kTile - 1) {   // whole tile inside the cache: row offsets step by 2 keys
+        const uint32_t r0 = __umul24((uint32_t)(16 * wu + hb), key_bytes);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = 16 * wu + 2 * i + (ln >> 5);
-        const int key = min(max(k0 + row, 0), a.n_kv - 1);
-        dma16(codes_b + (int64_t)key * a.Hkv * kD + 16 * ((ln & 31) ^ (row & 15)),
-              base + (16 * wu + 2 * i) * 512);
+        for (int i = 0; i < 8; ++i)
+          dma16_off(cb, r0 + 2 * i * key_bytes + (x ^ (32 * i)), base + (16 * wu + 2 * i) * 512);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int row = 16 * wu + 2 * i + hb;
+          dma16_off(cb, __umul24((uint32_t)min(row, last), key_bytes) + (x ^ (32 * i)),
+                    base + (16 * wu + 2 * i) * 512);
+        }
       }
       if (wu < 2) {
         const int row = 32 * wu + (ln >> 1);
-        const int key = min(max(k0 + row, 0), a.n_kv - 1);
-        dma16(scales_b + (int64_t)key * a.Hkv * (kD / 32) + 8 * (ln & 1), base + kCodeBytes + wu * 1024);
+        const char* sb = uniform_ptr((const char*)scales_b + (int64_t)k0 * key_sbytes);
+        dma16_off(sb, __umul24((uint32_t)min(row, last), key_sbytes) + 16 * (ln & 1), base + kCodeBytes + wu * 1024);
       }
       if (tab_tile && wu == 2 && ln < 32) {   // hi row of the tile (512 bytes: lanes 0..31)
         const int hr = (int)((int64_t)k0 % da.chunk >> 6);
-        dma16(da.rot_hi + (int64_t)hr * half_rot + 2 * ln, base + kHiRow);
+        dma16_off(uniform_ptr((const char*)(da.rot_hi + (int64_t)hr * half_rot)), 16 * ln, base + kHiRow);
       }
     };
     issue(0, kt0 * kTile);
@@ -318,16 +321,16 @@ __global__ __launch_bounds__(256, 2) void attn_decode_q8_kernel(DecodeArgs da) {
         const f16x8 pb = *(const f16x8*)(pbuf + lh * kTile + 32 * ks + 8 * lg);
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
-          // scales of block 4w + bb for keys 32 ks + 8 gq .. +7, as pairs
+          // the block's scale goes with the weights: P[h][key] * d[key][4w + bb] for keys
+          // 32 ks + 8 gq .. +7 (the values are then the exact integer codes)
           const f16x8 d8 = *(const f16x8*)(sT + (4 * w + bb) * kTile + 32 * ks + 8 * lg);
-          const f16x2 dd[4] = {{d8[0], d8[1]}, {d8[2], d8[3]}, {d8[4], d8[5]}, {d8[6], d8[7]}};
+          const f16x8 pd = pb * d8;
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const int dt = 2 * bb + h;
             const v2i c = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                 (lds_v2i*)(lds_char*)(vrow + 32 * ks * 512 + 16 * (pv_x ^ dt)));
-            const f16x8 vf = dequant8_keys((uint32_t)c[0], (uint32_t)c[1], dd);
-            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pb, o[dt], 0, 0, 0);
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8((uint32_t)c[0], (uint32_t)c[1]), pd, o[dt], 0, 0, 0);
           }
         }
       }
