@@ -3,8 +3,8 @@
 One step = one dca_attention call (remap, query rotation x3, key rotation, the three regime passes,
 the N-way merge) on the 32k-token prefill workload (one global layer: 16 query heads, 2 KV heads,
 head_dim 512, chunk 8192, bf16, inputs resident in HBM).  The 256k-KV decode workload (8 sequences,
-chunk 65536) is timed as a second leg, and the same decode over a q8_0 key cache as a third.  Prints
-one JSON line.
+chunk 65536) is timed as a second leg, and the same decode over q8_0 and q4_0 key caches as third and
+fourth legs.  Prints one JSON line.
 
 value: query tokens per second of the prefill workload.  roofline: the regime-pass kernel, timed
 live with HIP events recorded by the library between its stages, against the bf16 MFMA peak
@@ -50,11 +50,13 @@ class HipEvents:
         return float(out.value)
 
 
-def measured_traffic(kernel_file):
+def measured_traffic(kernel_file, workload=None):
     """HBM bytes per launch of a kernel, from the FETCH_SIZE/WRITE_SIZE counter passes recorded in
-    profiles/traffic.json; None when the kernel source changed since the counters were taken."""
+    profiles/traffic.json (keyed by the source file, or "file:workload" for a file with several
+    kernels); None when the kernel source changed since the counters were taken."""
+    key = kernel_file if workload is None else f"{kernel_file}:{workload}"
     try:
-        rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))[kernel_file]
+        rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))[key]
         src = open(os.path.join(ROOT, "dual_chunk_attention_amd", "csrc", kernel_file), "rb").read()
     except (OSError, KeyError, ValueError):
         return None
@@ -72,11 +74,12 @@ def to_dev(torch, a):
 def algorithmic_work(w):
     """Prefill: 4*D*Hq FLOP per attended (query, key) pair (QK^T and PV, every pair once across
     the three regimes).  Decode: the cache read once (K = V): B*N*Hkv*D*2 bytes for bf16,
-    B*N*Hkv*(D + 2*D/32) for q8_0 (one int8 code per dim, one fp16 scale per 32 dims)."""
+    B*N*Hkv*(D + 2*D/32) for q8_0 (one int8 code per dim, one fp16 scale per 32 dims) and
+    B*N*Hkv*(D/2 + 2*D/32) for q4_0 (4-bit codes)."""
     i = w.q0 + np.arange(w.T, dtype=np.float64)
     pairs = float(np.minimum(i + 1, w.N).sum()) * w.B
     flops = 4.0 * w.D * w.Hq * pairs
-    row_bytes = w.D + 2 * (w.D // 32) if w.dtype == "q8_0" else w.D * 2
+    row_bytes = {"q8_0": w.D + 2 * (w.D // 32), "q4_0": w.D // 2 + 2 * (w.D // 32)}.get(w.dtype, w.D * 2)
     kv_bytes = float(w.B) * w.N * w.Hkv * row_bytes
     return flops, kv_bytes
 
@@ -85,10 +88,10 @@ def time_leg(torch, dca, w, inp, steps, warmup):
     cfg = dca.Config(head_dim=w.D, n_rot=w.n_rot, n_head_q=w.Hq, n_head_kv=w.Hkv, chunk=w.chunk,
                      rope_theta=w.theta, scale=w.scale, freq_factors=to_dev(torch, inp["freq_factors"]))
     q, qp = to_dev(torch, inp["q"]), to_dev(torch, inp["q_pos"])
-    if w.dtype == "q8_0":
+    if w.dtype in ("q8_0", "q4_0"):
         k = (to_dev(torch, inp["k_codes"]), to_dev(torch, inp["k_scales"].view(np.int16)))
         ws_bytes = dca.attention_q8_workspace_size(cfg, w.B, w.T, w.N)
-        call = dca.attention_q8
+        call = dca.attention_q8 if w.dtype == "q8_0" else dca.attention_q4
     else:
         k = (to_dev(torch, inp["k"]),)
         ws_bytes = dca.attention_workspace_size(cfg, q.dtype, w.B, w.T, w.N)
@@ -199,7 +202,9 @@ def main():
     ap.add_argument("--decode-workload", default="decode-b8-kv256k-c65536")
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--q8-workload", default="decode-b8-kv256k-c65536-q8")
+    ap.add_argument("--q4-workload", default="decode-b8-kv256k-c65536-q4")
     ap.add_argument("--no-q8", action="store_true")
+    ap.add_argument("--no-q4", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -263,20 +268,23 @@ def main():
                           "regime_passes": std[3], "merge": std[4]},
         }
         del inpd
-    if not args.no_q8:
-        wq = synth.WORKLOADS[args.q8_workload]
+    for fmt, name in (("q8", args.q8_workload), ("q4", args.q4_workload)):
+        if getattr(args, "no_" + fmt):
+            continue
+        wq = synth.WORKLOADS[name]
         inpq = synth.make_inputs(wq)
         msq, stq = time_leg(torch, dca, wq, inpq, args.decode_steps, args.warmup)
-        _, q8_bytes = algorithmic_work(wq)
-        gbps = q8_bytes / (stq[3] * 1e-3) / 1e9
-        rec["decode_q8"] = {
+        _, q_bytes = algorithmic_work(wq)
+        gbps = q_bytes / (stq[3] * 1e-3) / 1e9
+        rec["decode_" + fmt] = {
             "workload": wq.name, "value": wq.B * wq.T / (msq * 1e-3), "unit": "tokens/s",
             "ms_per_step": msq, "steps": args.decode_steps,
             "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": gbps / HBM_PEAK_GBPS,
-                         "traffic": measured_traffic("attn_decode_q8.hip") if wq.name == "decode-b8-kv256k-c65536-q8" else None,
-                         "kernel": "attn_decode_q8_kernel (split-KV over the q8_0 cache, 3 regimes)",
-                         "kernel_ms": stq[3], "algorithmic_bytes": q8_bytes},
+                         "traffic": measured_traffic("attn_decode_quant.hip", wq.name),
+                         "kernel": f"attn_decode_quant_kernel<{8 if fmt == 'q8' else 4}> (split-KV over the "
+                                   f"{wq.dtype} cache, 3 regimes)",
+                         "kernel_ms": stq[3], "algorithmic_bytes": q_bytes},
             "stages_ms": {"remap": stq[0], "rope_q": stq[1], "tables": stq[2],
                           "regime_passes": stq[3], "merge": stq[4]},
         }
@@ -297,10 +305,11 @@ def main():
             rd = rec["decode"]["roofline"]
             rd["measured_peak"] = pk["hbm_read_gbps"]
             rd["frac_of_measured_peak"] = rd["achieved"] / pk["hbm_read_gbps"]
-        if "decode_q8" in rec:
-            rq = rec["decode_q8"]["roofline"]
-            rq["measured_peak"] = pk["hbm_read_gbps"]
-            rq["frac_of_measured_peak"] = rq["achieved"] / pk["hbm_read_gbps"]
+        for key in ("decode_q8", "decode_q4"):
+            if key in rec:
+                rq = rec[key]["roofline"]
+                rq["measured_peak"] = pk["hbm_read_gbps"]
+                rq["frac_of_measured_peak"] = rq["achieved"] / pk["hbm_read_gbps"]
         rec["measured_peaks"] = pk
     if not args.no_cpu_baseline:
         inp = synth.make_inputs(w)

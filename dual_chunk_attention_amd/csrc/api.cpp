@@ -467,15 +467,11 @@ dca_status dca_attention(const dca_config* cfg, dca_dtype dtype, int32_t B, int3
   return hip_status(mark(5, stream), "stage event");
 }
 
-size_t dca_attention_q8_workspace_size(const dca_config* cfg, int32_t B, int32_t T, int32_t n_kv) {
-  if (check_config(cfg, DCA_BF16) || check_sizes(B, T, n_kv)) return 0;
-  return attention_layout(cfg, DCA_BF16, B, T, n_kv, true).total;
-}
-
-dca_status dca_attention_q8(const dca_config* cfg, int32_t B, int32_t T, const void* q,
-                            const int32_t* q_pos, const int8_t* k_codes, const uint16_t* k_scales,
-                            int32_t n_kv, dca_dtype o_dtype, void* o, float* lse, void* workspace,
-                            size_t ws_bytes, hipStream_t stream) {
+// dca_attention_q8 / dca_attention_q4: the split-KV decode path over a block-quantized cache
+static dca_status attention_quant(int bits, const dca_config* cfg, int32_t B, int32_t T, const void* q,
+                                  const int32_t* q_pos, const void* k_codes, const uint16_t* k_scales,
+                                  int32_t n_kv, dca_dtype o_dtype, void* o, float* lse, void* workspace,
+                                  size_t ws_bytes, hipStream_t stream) {
   dca_status st = check_config(cfg, DCA_BF16);
   if (st) return st;
   if ((st = check_sizes(B, T, n_kv))) return st;
@@ -530,7 +526,8 @@ dca_status dca_attention_q8(const dca_config* cfg, int32_t B, int32_t T, const v
   da.rot_lo = lo;
   da.rot_hi = hi;
   da.chunk = cfg->chunk;
-  if ((st = hip_status(dca::launch_attn_decode_q8(da, stream), "q8 decode attention launch")))
+  if ((st = hip_status(bits == 8 ? dca::launch_attn_decode_q8(da, stream) : dca::launch_attn_decode_q4(da, stream),
+                       "quantized decode attention launch")))
     return st;
   if ((st = hip_status(mark(4, stream), "stage event"))) return st;
   dca::MergeArgs m{};
@@ -547,6 +544,31 @@ dca_status dca_attention_q8(const dca_config* cfg, int32_t B, int32_t T, const v
   if ((st = hip_status(dca::launch_merge_many(m, o_dtype == DCA_BF16, stream), "split merge launch")))
     return st;
   return hip_status(mark(5, stream), "stage event");
+}
+
+size_t dca_attention_q8_workspace_size(const dca_config* cfg, int32_t B, int32_t T, int32_t n_kv) {
+  if (check_config(cfg, DCA_BF16) || check_sizes(B, T, n_kv)) return 0;
+  return attention_layout(cfg, DCA_BF16, B, T, n_kv, true).total;
+}
+
+size_t dca_attention_q4_workspace_size(const dca_config* cfg, int32_t B, int32_t T, int32_t n_kv) {
+  return dca_attention_q8_workspace_size(cfg, B, T, n_kv);
+}
+
+dca_status dca_attention_q8(const dca_config* cfg, int32_t B, int32_t T, const void* q,
+                            const int32_t* q_pos, const int8_t* k_codes, const uint16_t* k_scales,
+                            int32_t n_kv, dca_dtype o_dtype, void* o, float* lse, void* workspace,
+                            size_t ws_bytes, hipStream_t stream) {
+  return attention_quant(8, cfg, B, T, q, q_pos, k_codes, k_scales, n_kv, o_dtype, o, lse, workspace,
+                         ws_bytes, stream);
+}
+
+dca_status dca_attention_q4(const dca_config* cfg, int32_t B, int32_t T, const void* q,
+                            const int32_t* q_pos, const uint8_t* k_codes, const uint16_t* k_scales,
+                            int32_t n_kv, dca_dtype o_dtype, void* o, float* lse, void* workspace,
+                            size_t ws_bytes, hipStream_t stream) {
+  return attention_quant(4, cfg, B, T, q, q_pos, k_codes, k_scales, n_kv, o_dtype, o, lse, workspace,
+                         ws_bytes, stream);
 }
 
 dca_status dca_probe_mfma_bf16(int32_t n_workgroups, int32_t iters, float* sink, hipStream_t stream) {

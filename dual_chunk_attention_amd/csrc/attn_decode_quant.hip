@@ -1,27 +1,32 @@
-// Split-KV regime passes for decode over a q8_0 key cache, on gfx950.
+// Split-KV regime passes for decode over a quantized key cache (q8_0 or q4_0), on gfx950.
 //
 // Same math as the bf16 decode passes (DCA feature page, "DCA algorithm", "Implementation
-// progress + Section-D simplification", "Section C2b"), over keys stored as q8_0 blocks: every 32
-// consecutive dims of a (key, KV head) row share one fp16 scale d, and the value of a dim is
-// d * q with q its int8 code (the pages run DCA over such caches, reading the codes inside the
-// kernel: Upstream Sync entry "0119-p0-dcaon-scalar-inregister").  The cache is read once, at
-// 544 bytes per key and head instead of 1024:
+// progress + Section-D simplification", "Section C2b"), over keys stored in blocks of 32
+// consecutive dims of a (key, KV head) row with one fp16 scale d each (the pages run DCA over such
+// caches, reading the codes inside the kernel: Upstream Sync entry
+// "0119-p0-dcaon-scalar-inregister").  q8_0: int8 codes q, value d * q (544 bytes per key and head
+// instead of 1024).  q4_0: 4-bit codes n packed two per byte in dim order (dim 2j in the low nibble
+// of byte j), value d * (n - 8) (288 bytes).
 //  * Each workgroup (4 waves) handles one (query row, KV head, span of keys) as in the bf16
-//    passes.  64-key tiles of codes (32 KiB) and scales (2 KiB) come in by direct global->LDS
-//    loads, double buffered; at ~78 KiB of LDS two workgroups share a CU.
+//    passes.  64-key tiles of codes (32 or 16 KiB) and scales (2 KiB) come in by direct
+//    global->LDS loads, double buffered; two workgroups share a CU.
 //  * No dequantized copy of the tile is stored.  The score operand (key rows, 8 dims per lane) is
 //    read as codes and turned into fp16 d*q in registers; the value operand (8 keys of one dim per
-//    lane) is read with gfx950's 8-bit transposing LDS read as exact integer codes, and each key's
-//    block scale multiplies its probability instead (from a small transposed copy of the tile's
-//    scales).  Both products run as fp16 MFMA 16x16x32 (the query's raw dims are converted from
-//    bf16 to fp16 once per row, the probabilities are fp16).
+//    lane) is read with gfx950's 8-bit transposing LDS read as exact integer codes (q4_0: one read
+//    gives two dims, the low and the high nibbles), and each key's block scale multiplies its
+//    probability instead (from a small transposed copy of the tile's scales).  Both products run
+//    as fp16 MFMA 16x16x32 (the query's raw dims are converted from bf16 to fp16 once per row, the
+//    probabilities are fp16).
 //  * Code rows sit in LDS with their 16-byte chunks XOR-swizzled by the row's low 4 bits (the
 //    loads pick the global chunk that belongs at each position), so that both the 16-row score
 //    reads and the 8-row transposing reads hit 16 distinct chunk slots.
 //  * The rotary dims of a key are rotated in registers at j mod c from the fp64-built cos/sin
 //    tables (lo[p & 63] composed with hi[p >> 6]), as in the bf16 passes.
-//  * Codes to fp16: every int8 code is an exact fp16 integer (one conversion each); one fp16
-//    multiply by d gives d*q.
+//  * Codes to fp16, exactly: an int8 code by one sign-extending conversion; a 4-bit code n by
+//    placing it under the fp16 exponent of 1024 (bit pattern 0x6400 | n = 1024 + n) and
+//    subtracting 1032.  One fp16 multiply by d then gives the value (one rounding).
+//  * q4_0 score fragments hold their 8 dims in the order the nibble extraction yields,
+//    (0, 4, 1, 5, 2, 6, 3, 7); the query fragments are stored in the same order.
 #include "common.h"
 
 namespace dca {
@@ -29,11 +34,18 @@ namespace {
 
 constexpr int kD = 512;
 constexpr int kTile = 64;
-constexpr int kCodeBytes = kTile * kD;            // 32 KiB of int8 codes per tile
 constexpr int kScaleBytes = kTile * kD / 32 * 2;  // 2 KiB of fp16 scales per tile, [key][block]
-constexpr int kHiRow = kCodeBytes + kScaleBytes;  // hi table row of the tile
-constexpr int kStageBytes = kHiRow + 512;
 constexpr float kTau = 8.0f;
+
+// stage layout per code width: codes [64 rows][kRow bytes], scales, the tile's hi table row
+template <int BITS>
+struct QLayout {
+  static constexpr int kRow = kD * BITS / 8;             // 512 (q8_0) or 256 (q4_0) bytes per key
+  static constexpr int kCodeBytes = kTile * kRow;
+  static constexpr int kRowsPerLoad = 1024 / kRow;        // rows one 64-lane 16-byte load covers
+  static constexpr int kHiRow = kCodeBytes + kScaleBytes;
+  static constexpr int kStageBytes = kHiRow + 512;
+};
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef int v2i __attribute__((ext_vector_type(2)));
@@ -68,14 +80,60 @@ __device__ __forceinline__ f16x8 codes8(uint32_t lo, uint32_t hi) {
 }
 #pragma clang diagnostic pop
 
-// eight codes of one block times its scale d -> eight fp16 values d*q (one rounding)
-__device__ __forceinline__ f16x8 dequant8(uint32_t lo, uint32_t hi, _Float16 d) {
-  const f16x8 c = codes8(lo, hi);
-  const f16x8 dd = {d, d, d, d, d, d, d, d};
-  return c * dd;
+// eight 4-bit codes of one word (element e at bits 4e..4e+3) -> n - 8 as fp16, in the order
+// (0, 4, 1, 5, 2, 6, 3, 7): the pair (e, e + 4) sits at bits 4e and 4e + 16
+__device__ __forceinline__ f16x8 nibbles8(uint32_t w) {
+  const f16x2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  f16x8 out;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const f16x2 h = __builtin_bit_cast(f16x2, ((w >> (4 * k)) & 0x000F000Fu) | 0x64006400u) - off;
+    out[2 * k] = h[0];
+    out[2 * k + 1] = h[1];
+  }
+  return out;
 }
 
-__global__ __launch_bounds__(256, 2) void attn_decode_q8_kernel(DecodeArgs da) {
+// the low (HIGH = false) or high nibbles of eight bytes (byte i = key i) -> n - 8 as fp16 in key
+// order
+template <bool HIGH>
+__device__ __forceinline__ f16x8 nibble_col8(uint32_t lo, uint32_t hi) {
+  const uint32_t a = (HIGH ? lo >> 4 : lo) & 0x0F0F0F0Fu, b = (HIGH ? hi >> 4 : hi) & 0x0F0F0F0Fu;
+  const f16x2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  f16x2 h[4];
+  h[0] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, a, 0x04010400u)) - off;
+  h[1] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, a, 0x04030402u)) - off;
+  h[2] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, b, 0x04010400u)) - off;
+  h[3] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, b, 0x04030402u)) - off;
+  f16x8 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = h[i][0];
+    out[2 * i + 1] = h[i][1];
+  }
+  return out;
+}
+
+// position p of a q4_0 score fragment holds element perm4(p) of its 8 dims
+__device__ __forceinline__ constexpr int perm4(int p) { return (p >> 1) + 4 * (p & 1); }
+
+template <int BITS>
+__device__ __forceinline__ f16x8 order_frag(const f16x8& v) {
+  if constexpr (BITS == 8) {
+    return v;
+  } else {
+    f16x8 o;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) o[p] = v[perm4(p)];
+    return o;
+  }
+}
+
+template <int BITS>
+__global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da) {
+  using LY = QLayout<BITS>;
+  constexpr int kRow = LY::kRow, kCodeBytes = LY::kCodeBytes, kStageBytes = LY::kStageBytes;
+  constexpr int kHiRow = LY::kHiRow, kRpl = LY::kRowsPerLoad;
   const AttnArgs& a = da.base;
   __shared__ __attribute__((aligned(1024))) char stage[2 * kStageBytes];
   __shared__ __attribute__((aligned(16))) _Float16 pbuf[16 * kTile];   // P[head][key]
@@ -99,14 +157,15 @@ __global__ __launch_bounds__(256, 2) void attn_decode_q8_kernel(DecodeArgs da) {
   const bool head_ok = hcol < G;
   const int64_t rowhead = bt * a.Hq + (int64_t)g * G + (head_ok ? hcol : 0);
 
-  const int8_t* codes_b = (const int8_t*)a.k_raw + ((int64_t)b * a.n_kv * a.Hkv + g) * kD;
+  const char* codes_b = (const char*)a.k_raw + ((int64_t)b * a.n_kv * a.Hkv + g) * kRow;
   const uint16_t* scales_b = da.k_scales + ((int64_t)b * a.n_kv * a.Hkv + g) * (kD / 32);
   const int half_rot = a.n_rot / 2;   // 64
   const float scale_log2 = a.scale * kLog2e;
 
-  // query fragments (fp16): B operand lane l holds Q[head hcol][32 s + 8 gq .. +7]; the raw dims
-  // come in as bf16 and are converted once into registers, the rotated dims (s < 4, one set per
-  // regime) are read per tile from LDS (head h's 16-byte chunk c at position c ^ h)
+  // query fragments (fp16): B operand lane l holds Q[head hcol][32 s + 8 gq .. +7] (q4_0: in the
+  // fragment order); the raw dims come in as bf16 and are converted once into registers, the
+  // rotated dims (s < 4, one set per regime) are read per tile from LDS (head h's 16-byte chunk c
+  // at position c ^ h)
   f16x8 q[16];
   {
     const bf16* qt = (const bf16*)a.q_tail + rowhead * a.q_tail_hs + 8 * gq;
@@ -116,20 +175,23 @@ __global__ __launch_bounds__(256, 2) void attn_decode_q8_kernel(DecodeArgs da) {
       f16x8 h;
 #pragma unroll
       for (int e = 0; e < 8; ++e) h[e] = head_ok ? (_Float16)(float)v[e] : (_Float16)0.0f;
-      q[s] = h;
+      q[s] = order_frag<BITS>(h);
     }
   }
   const int qrow = 16 * w + hcol;   // the lane's key row in the score product
 
   // Key rotation from the tables (see the bf16 passes): with c a multiple of 64 the lane's lo
   // entries stay in registers and the tile's hi row travels to LDS with the tile's loads.
+  // Fragment position p of the rotary k-steps holds dim 32 s + 8 gq + dim_of(p).
+  auto dim_of = [](int p) { return BITS == 8 ? p : perm4(p); };
   const bool tab_tile = da.chunk % 64 == 0;
   float2 lo_q[16];
   if (tab_tile) {
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) lo_q[8 * s + e] = da.rot_lo[qrow * half_rot + 32 * s + 8 * gq + e];
+      for (int e = 0; e < 8; ++e)
+        lo_q[8 * s + e] = da.rot_lo[qrow * half_rot + 32 * s + 8 * gq + dim_of(e)];
   }
 
   for (int r = 0; r < 3; ++r) {
@@ -144,12 +206,12 @@ __global__ __launch_bounds__(256, 2) void attn_decode_q8_kernel(DecodeArgs da) {
       continue;
     }
     {
-      // thread t: head t >> 4, dims 8 (t & 15) .. +7 (fp16 bits)
+      // thread t: head t >> 4, dims 8 (t & 15) .. +7 (fp16 bits, stored in the fragment order)
       const int h = tid >> 4, c = tid & 15;
-      bf16x8 v{};
+      f16x8 v{};
       if (h < G)
-        v = *(const bf16x8*)((const bf16*)a.q_rot[r] + (bt * a.Hq + (int64_t)g * G + h) * a.q_rot_hs + 8 * c);
-      *(bf16x8*)(qsm + h * 256 + 16 * (c ^ h)) = v;
+        v = *(const f16x8*)((const bf16*)a.q_rot[r] + (bt * a.Hq + (int64_t)g * G + h) * a.q_rot_hs + 8 * c);
+      *(f16x8*)(qsm + h * 256 + 16 * (c ^ h)) = order_frag<BITS>(v);
     }
     f32x4 o[8];
 #pragma unroll
@@ -160,7 +222,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_q8_kernel(DecodeArgs da) {
 
     const int kt0 = lo / kTile, kt1 = hi / kTile;
     // tile k0..k0+63 by direct global->LDS loads into stage buf: wave w the code rows
-    // 16w..16w+15 (two 512-byte rows per load; position p of row r receives global chunk
+    // 16w..16w+15 (kRpl rows of kRow bytes per load; position p of row r receives global chunk
     // p ^ (r & 15)), waves 0 and 1 the scale rows 0..31 and 32..63 (lane l the half l%2 of row
     // l/2), lanes 0..31 of wave 2 the hi table row; rows past the cache re-read its last key
     // (their scores are masked)
@@ -168,23 +230,24 @@ __global__ __launch_bounds__(256, 2) void attn_decode_q8_kernel(DecodeArgs da) {
       const uint32_t base = stage_lds + buf * kStageBytes;
       const int ln = opaque(l);
       const int last = a.n_kv - 1 - k0;   // the tile's last row inside the cache
-      const uint32_t key_bytes = (uint32_t)a.Hkv * kD, key_sbytes = (uint32_t)a.Hkv * (kD / 32) * 2;
-      const char* cb = uniform_ptr((const char*)codes_b + (int64_t)k0 * key_bytes);
-      // row 16 wu + 2 i + hb (hb = ln >> 5) has swizzle key 2 i + hb = 2 i ^ hb, so the lane's
-      // chunk offset is x ^ 32 i with x = 16 ((ln & 31) ^ hb)
-      const int hb = ln >> 5;
-      const uint32_t x = 16 * ((ln & 31) ^ hb);
-      if (last >= kTile - 1) {   // whole tile inside the cache: row offsets step by 2 keys
+      const uint32_t key_bytes = (uint32_t)a.Hkv * kRow, key_sbytes = (uint32_t)a.Hkv * (kD / 32) * 2;
+      const char* cb = uniform_ptr(codes_b + (int64_t)k0 * key_bytes);
+      // row 16 wu + kRpl i + hb (hb = the lane's row within the load) has swizzle key
+      // kRpl i + hb = kRpl i ^ hb, so the lane's chunk offset is x ^ 16 kRpl i
+      constexpr int kLanesPerRow = 64 / kRpl;
+      const int hb = ln / kLanesPerRow;
+      const uint32_t x = 16 * ((ln % kLanesPerRow) ^ hb);
+      if (last >= kTile - 1) {   // whole tile inside the cache: row offsets step by kRpl keys
         const uint32_t r0 = __umul24((uint32_t)(16 * wu + hb), key_bytes);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          dma16_off(cb, r0 + 2 * i * key_bytes + (x ^ (32 * i)), base + (16 * wu + 2 * i) * 512);
+        for (int i = 0; i < 16 / kRpl; ++i)
+          dma16_off(cb, r0 + kRpl * i * key_bytes + (x ^ (16 * kRpl * i)), base + (16 * wu + kRpl * i) * kRow);
       } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int row = 16 * wu + 2 * i + hb;
-          dma16_off(cb, __umul24((uint32_t)min(row, last), key_bytes) + (x ^ (32 * i)),
-                    base + (16 * wu + 2 * i) * 512);
+        for (int i = 0; i < 16 / kRpl; ++i) {
+          const int row = 16 * wu + kRpl * i + hb;
+          dma16_off(cb, __umul24((uint32_t)min(row, last), key_bytes) + (x ^ (16 * kRpl * i)),
+                    base + (16 * wu + kRpl * i) * kRow);
         }
       }
       if (wu < 2) {
@@ -211,15 +274,11 @@ __global__ __launch_bounds__(256, 2) void attn_decode_q8_kernel(DecodeArgs da) {
       const int ln = opaque(l);
       const int lh = ln & 15, lg = ln >> 4;
       const int lrow = 16 * w + lh;
-      // score operand: key row lrow (swizzle key lh), 8 dims at 32 s + 8 lg: chunk 2 s + (lg >> 1)
-      const char* kq = st + lrow * 512 + 8 * (lg & 1);
-      const int kq_x = (lg >> 1) ^ lh;
-      // value operand: transposing reads of rows 32 ks + 8 lg + (lh >> 1), bytes 8 (lh & 1) of the
-      // chunk of dims 128 w + 16 dt; swizzle key = the row's low 4 bits = 8 (lg & 1) + (lh >> 1),
-      // and with dt < 8: (8 w + dt) ^ key = ((8 w) ^ key) ^ dt
+      // value operand: transposing reads of rows 32 ks + 8 lg + (lh >> 1), bytes 8 (lh & 1) of a
+      // 16-byte chunk; swizzle key = the row's low 4 bits = 8 (lg & 1) + (lh >> 1)
       const int pv_row = 8 * lg + (lh >> 1);
-      const char* vrow = st + pv_row * 512 + 8 * (lh & 1);
-      const int pv_x = (8 * w) ^ (pv_row & 15);
+      const char* vrow = st + pv_row * kRow + 8 * (lh & 1);
+      const int pv_key = pv_row & 15;
 
       // ---- scales: the lane's key row for the scores, and the transposed copy for the values
       f16x8 dsc[2];
@@ -236,8 +295,17 @@ __global__ __launch_bounds__(256, 2) void attn_decode_q8_kernel(DecodeArgs da) {
 
       // ---- S^T for keys [16w, 16w+16): codes -> fp16 d*q in registers ------------------------
       auto kfrag = [&](int s) {
-        const uint2 c8 = *(const uint2*)(kq + 16 * ((2 * s) ^ kq_x));
-        return dequant8(c8.x, c8.y, dsc[s >> 3][s & 7]);
+        const _Float16 d = dsc[s >> 3][s & 7];
+        const f16x8 dd = {d, d, d, d, d, d, d, d};
+        if constexpr (BITS == 8) {
+          // dims 32 s + 8 lg .. +7: chunk 2 s + (lg >> 1), bytes 8 (lg & 1)
+          const uint2 c8 = *(const uint2*)(st + lrow * kRow + 8 * (lg & 1) + 16 * ((2 * s + (lg >> 1)) ^ lh));
+          return codes8(c8.x, c8.y) * dd;
+        } else {
+          // dims 32 s + 8 lg .. +7: chunk s, bytes 4 lg
+          const uint32_t c4 = *(const uint32_t*)(st + lrow * kRow + 4 * lg + 16 * (s ^ lh));
+          return nibbles8(c4) * dd;
+        }
       };
       f32x4 sacc = f32x4{};
       {
@@ -252,7 +320,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_q8_kernel(DecodeArgs da) {
             __builtin_amdgcn_sched_barrier(0);   // one half at a time: bounds the live table entries
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const int f = 32 * s + 8 * gq + e;
+              const int f = 32 * s + 8 * gq + dim_of(e);
               const float2 A = lo_of(8 * s + e, f), Bv = hi_of(f);
               const float cs = A.x * Bv.x - A.y * Bv.y;
               const float sn = A.y * Bv.x + A.x * Bv.y;
@@ -316,21 +384,34 @@ __global__ __launch_bounds__(256, 2) void attn_decode_q8_kernel(DecodeArgs da) {
       __syncthreads();
 
       // ---- O^T += V^T P^T for dims [128w, 128w+128) ------------------------------------------
+      // q8_0: o[dt] holds dims 128 w + 16 dt + (4 gq .. +3); q4_0: o[2 bb] and o[2 bb + 1] hold
+      // the even and odd dims 128 w + 32 bb + 8 gq + (0, 2, 4, 6) and (1, 3, 5, 7)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const f16x8 pb = *(const f16x8*)(pbuf + lh * kTile + 32 * ks + 8 * lg);
+        const char* vr = vrow + 32 * ks * kRow;
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
           // the block's scale goes with the weights: P[h][key] * d[key][4w + bb] for keys
           // 32 ks + 8 gq .. +7 (the values are then the exact integer codes)
           const f16x8 d8 = *(const f16x8*)(sT + (4 * w + bb) * kTile + 32 * ks + 8 * lg);
           const f16x8 pd = pb * d8;
+          if constexpr (BITS == 8) {
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int dt = 2 * bb + h;
+            for (int h = 0; h < 2; ++h) {
+              const int dt = 2 * bb + h;   // chunk 8 w + dt
+              const v2i c = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                  (lds_v2i*)(lds_char*)(vr + 16 * ((8 * w + dt) ^ pv_key)));
+              o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8((uint32_t)c[0], (uint32_t)c[1]), pd, o[dt], 0, 0, 0);
+            }
+          } else {
+            // chunk 4 w + bb = block 4 w + bb: byte i of the chunk holds dims 2 i and 2 i + 1
             const v2i c = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (lds_v2i*)(lds_char*)(vrow + 32 * ks * 512 + 16 * (pv_x ^ dt)));
-            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8((uint32_t)c[0], (uint32_t)c[1]), pd, o[dt], 0, 0, 0);
+                (lds_v2i*)(lds_char*)(vr + 16 * ((4 * w + bb) ^ pv_key)));
+            o[2 * bb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                nibble_col8<false>((uint32_t)c[0], (uint32_t)c[1]), pd, o[2 * bb], 0, 0, 0);
+            o[2 * bb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                nibble_col8<true>((uint32_t)c[0], (uint32_t)c[1]), pd, o[2 * bb + 1], 0, 0, 0);
           }
         }
       }
@@ -352,25 +433,38 @@ __global__ __launch_bounds__(256, 2) void attn_decode_q8_kernel(DecodeArgs da) {
     const bool nonempty = l_tot > 0.0f && w_tot > 0.0f;
     const float inv = nonempty ? 1.0f / w_tot : 0.0f;
     if (head_ok) {
-      float* orow = da.o_part + ((int64_t)slot * rows * a.Hq + rowhead) * kD + 128 * w + 4 * gq;
+      float* orow = da.o_part + ((int64_t)slot * rows * a.Hq + rowhead) * kD + 128 * w;
+      if constexpr (BITS == 8) {
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) *(f32x4*)(orow + 16 * dt) = o[dt] * inv;
+        for (int dt = 0; dt < 8; ++dt) *(f32x4*)(orow + 16 * dt + 4 * gq) = o[dt] * inv;
+      } else {
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          const f32x4 ev = o[2 * bb] * inv, od = o[2 * bb + 1] * inv;
+          *(f32x4*)(orow + 32 * bb + 8 * gq) = f32x4{ev[0], od[0], ev[1], od[1]};
+          *(f32x4*)(orow + 32 * bb + 8 * gq + 4) = f32x4{ev[2], od[2], ev[3], od[3]};
+        }
+      }
       if (gq == 0 && w == 0) lse_out[rowhead] = nonempty ? (m_used + log2f(l_tot)) * kLn2 : -INFINITY;
     }
     __syncthreads();
   }
 }
 
-}  // namespace
-
-hipError_t launch_attn_decode_q8(const DecodeArgs& a, hipStream_t stream) {
+template <int BITS>
+hipError_t launch_quant(const DecodeArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.base.B * a.base.T;
   if (rows <= 0 || a.n_spans <= 0) return hipSuccess;
   if (!a.rot_lo || !a.base.rot_f16 || (a.base.n_kv > 0 && (!a.k_scales || !a.base.k_raw)))
     return hipErrorInvalidValue;
   dim3 grid((unsigned)a.n_spans, (unsigned)(rows * a.base.Hkv)), block(256);
-  hipLaunchKernelGGL(attn_decode_q8_kernel, grid, block, 0, stream, a);
+  hipLaunchKernelGGL(attn_decode_quant_kernel<BITS>, grid, block, 0, stream, a);
   return hipGetLastError();
 }
+
+}  // namespace
+
+hipError_t launch_attn_decode_q8(const DecodeArgs& a, hipStream_t stream) { return launch_quant<8>(a, stream); }
+hipError_t launch_attn_decode_q4(const DecodeArgs& a, hipStream_t stream) { return launch_quant<4>(a, stream); }
 
 }  // namespace dca

@@ -179,12 +179,13 @@ struct DecodeArgs {
   const float2* rot_hi;
   int32_t chunk;
   double theta;
-  // q8_0 key cache (launch_attn_decode_q8): base.k_raw holds the int8 codes [B,N,Hkv,D] and
-  // k_scales the fp16 block scales [B,N,Hkv,D/32]
+  // quantized key cache: base.k_raw holds the codes (q8_0: int8 [B,N,Hkv,D]; q4_0: uint8
+  // [B,N,Hkv,D/2], two 4-bit codes per byte) and k_scales the fp16 block scales [B,N,Hkv,D/32]
   const uint16_t* k_scales;
 };
 hipError_t launch_attn_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_attn_decode_q8(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_attn_decode_q4(const DecodeArgs& a, hipStream_t stream);
 
 // reference-rate probes (calibrate.hip)
 hipError_t launch_probe_mfma(int32_t n_workgroups, int32_t iters, float* sink, hipStream_t stream);

@@ -64,13 +64,16 @@ def lib():
                                        sz, vp]
         L.dca_attention_q8_workspace_size.argtypes = [cfgp, i32, i32, i32]
         L.dca_attention_q8_workspace_size.restype = sz
+        L.dca_attention_q4.argtypes = L.dca_attention_q8.argtypes
+        L.dca_attention_q4_workspace_size.argtypes = [cfgp, i32, i32, i32]
+        L.dca_attention_q4_workspace_size.restype = sz
         L.dca_set_stage_events.argtypes = [vp, i32]
         L.dca_set_stage_events.restype = ctypes.c_int
         L.dca_last_error.restype = ctypes.c_char_p
         L.dca_probe_mfma_bf16.argtypes = [i32, i32, vp, vp]
         L.dca_probe_hbm_read.argtypes = [vp, i64, i32, vp, vp]
         for f in ("dca_remap_positions", "dca_rope_partial", "dca_attn_regime", "dca_lse_merge",
-                  "dca_attention", "dca_attention_q8", "dca_probe_mfma_bf16", "dca_probe_hbm_read"):
+                  "dca_attention", "dca_attention_q8", "dca_attention_q4", "dca_probe_mfma_bf16", "dca_probe_hbm_read"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -218,6 +221,35 @@ def attention_q8_workspace_size(cfg: Config, B: int, T: int, n_kv: int) -> int:
     return int(lib().dca_attention_q8_workspace_size(ctypes.byref(c), B, T, n_kv))
 
 
+def attention_q4_workspace_size(cfg: Config, B: int, T: int, n_kv: int) -> int:
+    c = cfg.c()
+    return int(lib().dca_attention_q4_workspace_size(ctypes.byref(c), B, T, n_kv))
+
+
+def _attention_quant(fn, ws_fn, per_byte, code_dtypes, cfg, q, q_pos, k_codes, k_scales, o_dtype,
+                     workspace, out, lse):
+    B, T, Hq, D = q.shape
+    N = k_codes.shape[1]
+    assert q.dtype == torch.bfloat16 and q_pos.dtype == torch.int32
+    assert k_codes.dtype in code_dtypes and k_scales.dtype in (torch.float16, torch.int16)
+    assert k_codes.shape[3] * per_byte == D
+    assert k_scales.shape == (*k_codes.shape[:3], D // 32)
+    assert q.is_contiguous() and q_pos.is_contiguous()
+    assert k_codes.is_contiguous() and k_scales.is_contiguous()
+    od = o_dtype or torch.bfloat16
+    c = cfg.c()
+    ws_bytes = ws_fn(ctypes.byref(c), B, T, N)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, T, Hq, D), dtype=od, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device)
+    _check(fn(ctypes.byref(c), B, T, _ptr(q), _ptr(q_pos), _ptr(k_codes), _ptr(k_scales), N,
+              _dtype_code(od), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream()))
+    return out, lse
+
+
 def attention_q8(cfg: Config, q: torch.Tensor, q_pos: torch.Tensor, k_codes: torch.Tensor,
                  k_scales: torch.Tensor, o_dtype: Optional[torch.dtype] = None,
                  workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
@@ -225,26 +257,20 @@ def attention_q8(cfg: Config, q: torch.Tensor, q_pos: torch.Tensor, k_codes: tor
     """dca_attention_q8: q bf16 [B,T,Hq,D], q_pos int32 [B,T], q8_0 key cache (K = V) as int8
     codes [B,N,Hkv,D] and fp16 scales [B,N,Hkv,D/32] (the scales' raw bits may also come as int16)
     -> (o [B,T,Hq,D] of o_dtype (default bf16), lse fp32 [B,T,Hq])."""
-    B, T, Hq, D = q.shape
-    N = k_codes.shape[1]
-    assert q.dtype == torch.bfloat16 and q_pos.dtype == torch.int32
-    assert k_codes.dtype == torch.int8 and k_scales.dtype in (torch.float16, torch.int16)
-    assert k_scales.shape == (*k_codes.shape[:3], k_codes.shape[3] // 32)
-    assert q.is_contiguous() and q_pos.is_contiguous()
-    assert k_codes.is_contiguous() and k_scales.is_contiguous()
-    od = o_dtype or torch.bfloat16
-    c = cfg.c()
-    ws_bytes = lib().dca_attention_q8_workspace_size(ctypes.byref(c), B, T, N)
-    if workspace is None or workspace.numel() < ws_bytes:
-        workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty((B, T, Hq, D), dtype=od, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device)
-    _check(lib().dca_attention_q8(ctypes.byref(c), B, T, _ptr(q), _ptr(q_pos), _ptr(k_codes),
-                                  _ptr(k_scales), N, _dtype_code(od), _ptr(out), _ptr(lse),
-                                  _ptr(workspace), workspace.numel(), _stream()))
-    return out, lse
+    L = lib()
+    return _attention_quant(L.dca_attention_q8, L.dca_attention_q8_workspace_size, 1, (torch.int8,),
+                            cfg, q, q_pos, k_codes, k_scales, o_dtype, workspace, out, lse)
+
+
+def attention_q4(cfg: Config, q: torch.Tensor, q_pos: torch.Tensor, k_codes: torch.Tensor,
+                 k_scales: torch.Tensor, o_dtype: Optional[torch.dtype] = None,
+                 workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                 lse: Optional[torch.Tensor] = None):
+    """dca_attention_q4: as attention_q8 over a q4_0 key cache: codes uint8 [B,N,Hkv,D/2] (dim 2j
+    in the low nibble of byte j) and fp16 scales [B,N,Hkv,D/32]."""
+    L = lib()
+    return _attention_quant(L.dca_attention_q4, L.dca_attention_q4_workspace_size, 2, (torch.uint8,),
+                            cfg, q, q_pos, k_codes, k_scales, o_dtype, workspace, out, lse)
 
 
 N_STAGE_EVENTS = 6

@@ -190,6 +190,22 @@ dca_status dca_attention_q8(const dca_config* cfg, int32_t B, int32_t T, const v
                             size_t ws_bytes, hipStream_t stream);
 size_t dca_attention_q8_workspace_size(const dca_config* cfg, int32_t B, int32_t T, int32_t n_kv);
 
+/* dca_attention_q8 over a key cache stored as q4_0 blocks (named with q8_0 among the scalar cache
+ * types the pages read in registers inside the DCA kernel, Upstream Sync entry
+ * "0119-p0-dcaon-scalar-inregister", and as the value half of their q8_0-K / q4_0-V pairs; no
+ * layout printed).  Every 32 consecutive dims of one (key, KV head) row share an fp16 scale d; a
+ * dim's value is d * (n - 8) with n its 4-bit code in [0, 15].
+ * k_codes : uint8 [B,n_kv,Hkv,D/2]: dim 2j of a row in the low nibble of byte j, dim 2j+1 in the
+ *           high nibble (this packing order is the library's; the pages fix none).
+ * k_scales: fp16 bit patterns [B,n_kv,Hkv,D/32].
+ * Everything else (q, outputs, limits, errors, stage events) as dca_attention_q8.
+ * workspace: at least dca_attention_q4_workspace_size() bytes of device memory. */
+dca_status dca_attention_q4(const dca_config* cfg, int32_t B, int32_t T, const void* q,
+                            const int32_t* q_pos, const uint8_t* k_codes, const uint16_t* k_scales,
+                            int32_t n_kv, dca_dtype o_dtype, void* o, float* lse, void* workspace,
+                            size_t ws_bytes, hipStream_t stream);
+size_t dca_attention_q4_workspace_size(const dca_config* cfg, int32_t B, int32_t T, int32_t n_kv);
+
 /* Optional stage timing for dca_attention (measurement hook; no page defines it).  After
  * dca_set_stage_events(ev, n) with n >= DCA_N_STAGE_EVENTS, every dca_attention call made later on
  * this thread records, on its stream: ev[0] before the remap, ev[1] after the remap, ev[2] after

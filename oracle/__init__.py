@@ -56,6 +56,10 @@ def _lib():
         lib.dca_oracle_half.argtypes = [ctypes.c_uint16]
         lib.dca_oracle_dequant_q8.restype = None
         lib.dca_oracle_dequant_q8.argtypes = [ctypes.c_void_p, ctypes.c_void_p, i64, f64p]
+        lib.dca_oracle_attention_q4.restype = ctypes.c_int
+        lib.dca_oracle_attention_q4.argtypes = lib.dca_oracle_attention_q8.argtypes
+        lib.dca_oracle_dequant_q4.restype = None
+        lib.dca_oracle_dequant_q4.argtypes = [ctypes.c_void_p, ctypes.c_void_p, i64, f64p]
         _LIB = lib
     return _LIB
 
@@ -184,13 +188,23 @@ def dequant_q8(codes, scales):
     return out
 
 
-def attention_q8(q, qpos, codes, scales, *, chunk, n_rot, theta, scale, freq_factors=None, rows=None,
-                 per_regime=True, n_threads=0, remap_mode=REMAP_BASELINE):
-    """DCA attention (as `attention`) over a q8_0 key cache: codes int8 [B, N, Hkv, D], scales
-    uint16 fp16 bits [B, N, Hkv, D/32]; the keys (and values, K = V) are d * q.  q is float32 or
-    uint16 bf16 bits [B, T, Hq, D]."""
+def dequant_q4(codes, scales):
+    """Values d * (n - 8) of a q4_0 cache (reading in the header of dca_oracle.c): codes uint8
+    [..., D/2] (dim 2j in the low nibble of byte j), scales uint16 fp16 bits [..., D/32] ->
+    float64 [..., D]."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    assert codes.shape[:-1] == scales.shape[:-1] and 2 * codes.shape[-1] == 32 * scales.shape[-1]
+    out = np.empty(codes.shape[:-1] + (2 * codes.shape[-1],), np.float64)
+    _lib().dca_oracle_dequant_q4(codes.ctypes.data_as(ctypes.c_void_p), scales.ctypes.data_as(ctypes.c_void_p),
+                                 out.size, _ptr(out, ctypes.c_double))
+    return out
+
+
+def _attention_quant(fn, elems_per_byte, code_dtype, q, qpos, codes, scales, *, chunk, n_rot, theta,
+                     scale, freq_factors, rows, per_regime, n_threads, remap_mode):
     q = np.ascontiguousarray(q)
-    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    codes = np.ascontiguousarray(codes, dtype=code_dtype)
     scales = np.ascontiguousarray(scales, dtype=np.uint16)
     if q.dtype == np.uint16:
         q_bf16 = 1
@@ -200,7 +214,7 @@ def attention_q8(q, qpos, codes, scales, *, chunk, n_rot, theta, scale, freq_fac
         raise TypeError("q must be float32 or uint16 (bf16 bits)")
     B, T, Hq, D = q.shape
     Bk, N, Hkv, Dk = codes.shape
-    assert Bk == B and Dk == D and scales.shape == (B, N, Hkv, D // 32)
+    assert Bk == B and Dk * elems_per_byte == D and scales.shape == (B, N, Hkv, D // 32)
     qpos = np.ascontiguousarray(np.asarray(qpos, dtype=np.int32).reshape(B, T))
     sel = np.arange(B * T, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
     n = sel.size
@@ -209,7 +223,7 @@ def attention_q8(q, qpos, codes, scales, *, chunk, n_rot, theta, scale, freq_fac
     o_reg = np.zeros((3, n, Hq, D), np.float64) if per_regime else None
     lse_reg = np.zeros((3, n, Hq), np.float64) if per_regime else None
     ff = None if freq_factors is None else np.ascontiguousarray(freq_factors, dtype=np.float64)
-    st = _lib().dca_oracle_attention_q8(
+    st = fn(
         D, int(n_rot), Hq, Hkv, int(chunk), int(remap_mode), float(theta), float(scale),
         None if ff is None else _ptr(ff, ctypes.c_double), q_bf16, B, T,
         q.ctypes.data_as(ctypes.c_void_p), _ptr(qpos, ctypes.c_int32),
@@ -220,3 +234,22 @@ def attention_q8(q, qpos, codes, scales, *, chunk, n_rot, theta, scale, freq_fac
     if st != 0:
         raise RuntimeError(f"oracle attention failed with status {st}")
     return dict(o=o, lse=lse, o_reg=o_reg, lse_reg=lse_reg, rows=sel)
+
+
+def attention_q8(q, qpos, codes, scales, *, chunk, n_rot, theta, scale, freq_factors=None, rows=None,
+                 per_regime=True, n_threads=0, remap_mode=REMAP_BASELINE):
+    """DCA attention (as `attention`) over a q8_0 key cache: codes int8 [B, N, Hkv, D], scales
+    uint16 fp16 bits [B, N, Hkv, D/32]; the keys (and values, K = V) are d * q.  q is float32 or
+    uint16 bf16 bits [B, T, Hq, D]."""
+    return _attention_quant(_lib().dca_oracle_attention_q8, 1, np.int8, q, qpos, codes, scales,
+                            chunk=chunk, n_rot=n_rot, theta=theta, scale=scale, freq_factors=freq_factors,
+                            rows=rows, per_regime=per_regime, n_threads=n_threads, remap_mode=remap_mode)
+
+
+def attention_q4(q, qpos, codes, scales, *, chunk, n_rot, theta, scale, freq_factors=None, rows=None,
+                 per_regime=True, n_threads=0, remap_mode=REMAP_BASELINE):
+    """DCA attention (as `attention`) over a q4_0 key cache: codes uint8 [B, N, Hkv, D/2] (two
+    per byte), scales uint16 fp16 bits [B, N, Hkv, D/32]; the keys (and values) are d * (n - 8)."""
+    return _attention_quant(_lib().dca_oracle_attention_q4, 2, np.uint8, q, qpos, codes, scales,
+                            chunk=chunk, n_rot=n_rot, theta=theta, scale=scale, freq_factors=freq_factors,
+                            rows=rows, per_regime=per_regime, n_threads=n_threads, remap_mode=remap_mode)

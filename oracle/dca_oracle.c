@@ -56,6 +56,13 @@
  * value d * q exactly (fp16 -> double by the IEEE binary16 definition) and then runs the same
  * attention on it.
  *
+ * Quantized keys (q4_0): the pages name q4_0 beside q8_0 among the scalar cache types read in
+ * registers ([U] "0119-p0-dcaon-scalar-inregister", and the q8_0-K / q4_0-V pairs), again with no
+ * layout.  Reading: every 32 consecutive dims form a block with one fp16 scale d and 32 unsigned
+ * 4-bit codes n in [0, 15]; the value is d * (n - 8).  Codes are packed two per byte in dim order:
+ * dim 2j in the low nibble of byte j, dim 2j + 1 in the high nibble (uint8 [..][D/2]); scales as
+ * for q8_0.  This packing order is this file's reading (the pages fix none).
+ *
  * Scores s_j = scale * <rot(q, P_reg(j)), rot(k_j, j mod c)>, softmax over the union of the
  * regimes, O = sum_j softmax_j * k_j (un-rotated), LSE = m + ln sum_j e^(s_j - m).
  * Query head h uses KV head h / (Hq / Hkv).
@@ -202,8 +209,9 @@ double dca_oracle_half(uint16_t h) {
   return sign ? -v : v;
 }
 
-/* A key cache: fp32 (kind 0), bf16 bit patterns (kind 1) or q8_0 (kind 2: int8 codes in p, fp16
- * scale bits in scales, one per 32 consecutive elements of a row). */
+/* A key cache: fp32 (kind 0), bf16 bit patterns (kind 1), q8_0 (kind 2: int8 codes in p, fp16
+ * scale bits in scales, one per 32 consecutive elements of a row) or q4_0 (kind 3: 4-bit codes,
+ * element e in byte e / 2, low nibble for even e; same scales). */
 typedef struct {
   const void* p;
   const uint16_t* scales;
@@ -212,12 +220,23 @@ typedef struct {
 
 static double load_k(const kv_src* k, int64_t e) {
   if (k->kind == 2) return dca_oracle_half(k->scales[e / 32]) * (double)((const int8_t*)k->p)[e];
+  if (k->kind == 3) {
+    const int byte = ((const uint8_t*)k->p)[e / 2];
+    const int n = (e % 2 == 0) ? (byte & 15) : (byte >> 4);
+    return dca_oracle_half(k->scales[e / 32]) * (double)(n - 8);
+  }
   return load_in(k->p, e, k->kind);
 }
 
 /* Dequantized values of n elements of a q8_0 cache (codes + fp16 scales), for the tests. */
 void dca_oracle_dequant_q8(const int8_t* codes, const uint16_t* scales, int64_t n, double* out) {
   kv_src k = {codes, scales, 2};
+  for (int64_t e = 0; e < n; ++e) out[e] = load_k(&k, e);
+}
+
+/* Dequantized values of n elements of a q4_0 cache (codes packed two per byte + fp16 scales). */
+void dca_oracle_dequant_q4(const uint8_t* codes, const uint16_t* scales, int64_t n, double* out) {
+  kv_src k = {codes, scales, 3};
   for (int64_t e = 0; e < n; ++e) out[e] = load_k(&k, e);
 }
 
@@ -272,7 +291,7 @@ static int attention_impl(int64_t D, int64_t n_rot, int64_t Hq, int64_t Hkv, int
                           double* o_reg, double* lse_reg, int n_threads) {
   if (D <= 0 || n_rot <= 0 || n_rot > D || n_rot > 1024 || (n_rot & 1) || Hq <= 0 || Hkv <= 0 ||
       Hq % Hkv || c <= 0 || mode < 0 || mode > 2 || B <= 0 || T <= 0 || n_kv < 0 ||
-      (kv->kind == 2 && (D % 32 || !kv->scales)))
+      (kv->kind >= 2 && (D % 32 || !kv->scales)))
     return -2;
 #ifdef _OPENMP
   if (n_threads > 0) omp_set_num_threads(n_threads);
@@ -404,6 +423,18 @@ int dca_oracle_attention_q8(int64_t D, int64_t n_rot, int64_t Hq, int64_t Hkv, i
                             const uint16_t* scales, int64_t n_kv, int64_t n_sel, const int64_t* sel,
                             double* o, double* lse, double* o_reg, double* lse_reg, int n_threads) {
   kv_src kv = {codes, scales, 2};
+  return attention_impl(D, n_rot, Hq, Hkv, c, mode, theta, scale, ff, q_bf16, 0, B, T, q, qpos,
+                        &kv, n_kv, n_sel, sel, o, lse, o_reg, lse_reg, n_threads);
+}
+
+/* The same attention over a q4_0 key cache (codes uint8 [B][n_kv][Hkv][D/2], two per byte, scales
+ * fp16 bits [B][n_kv][Hkv][D/32]). */
+int dca_oracle_attention_q4(int64_t D, int64_t n_rot, int64_t Hq, int64_t Hkv, int64_t c, int mode,
+                            double theta, double scale, const double* ff, int q_bf16, int64_t B,
+                            int64_t T, const void* q, const int32_t* qpos, const uint8_t* codes,
+                            const uint16_t* scales, int64_t n_kv, int64_t n_sel, const int64_t* sel,
+                            double* o, double* lse, double* o_reg, double* lse_reg, int n_threads) {
+  kv_src kv = {codes, scales, 3};
   return attention_impl(D, n_rot, Hq, Hkv, c, mode, theta, scale, ff, q_bf16, 0, B, T, q, qpos,
                         &kv, n_kv, n_sel, sel, o, lse, o_reg, lse_reg, n_threads);
 }

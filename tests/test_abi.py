@@ -119,3 +119,19 @@ def test_q8_entry_point_validation():
                               1 << 40, None) == dca.ERR_UNSUPPORTED
     assert L.dca_attention_q8(ctypes.byref(c), 0, 1, None, None, None, None, 4, dca.BF16, None, None,
                               None, 0, None) == dca.OK
+
+
+def test_q4_entry_point_validation():
+    if not os.path.exists(dca.LIB_PATH):
+        pytest.skip("libdca.so not built")
+    L = dca.lib()
+    c = _cfg()
+    vp = ctypes.c_void_p(16)
+    need = L.dca_attention_q4_workspace_size(ctypes.byref(c), 8, 1, 262144)
+    assert need == L.dca_attention_q8_workspace_size(ctypes.byref(c), 8, 1, 262144) > 0
+    assert L.dca_attention_q4(ctypes.byref(c), 8, 1, vp, vp, vp, vp, 262144, dca.BF16, vp, None, vp,
+                              need - 1, None) == dca.ERR_WORKSPACE_TOO_SMALL
+    assert L.dca_attention_q4(ctypes.byref(c), 8, 1, vp, vp, None, vp, 262144, dca.BF16, vp, None, vp,
+                              need, None) == dca.ERR_INVALID_ARGUMENT     # codes missing
+    assert L.dca_attention_q4(ctypes.byref(c), 0, 1, None, None, None, None, 4, dca.BF16, None, None,
+                              None, 0, None) == dca.OK

@@ -1,5 +1,5 @@
-"""GPU parity of the decode over a q8_0 key cache (dca_attention_q8) against the fp64 oracle reading
-the same codes and scales.
+"""GPU parity of the decode over a q8_0 or q4_0 key cache (dca_attention_q8 / dca_attention_q4)
+against the fp64 oracle reading the same codes and scales.
 
 Bar as for the bf16 path: O within 1e-2 absolute, LSE within 1e-3 relative, an all-empty row
 exactly (0, -inf).  The kernel forms each key value d*q in fp16 (one rounding) and the rotated dims
@@ -15,31 +15,32 @@ from gpu_util import assert_lse_close, assert_o_close, cfg_for, dev, to_dev
 
 pytestmark = pytest.mark.gpu
 
-Q8 = "decode-b8-kv256k-c65536-q8"
+# format -> (full workload, GPU entry point, oracle, block store, dtype name)
+FORMATS = {
+    "q8": ("decode-b8-kv256k-c65536-q8", dca.attention_q8, oracle.attention_q8, synth.q8_0_blocks, "q8_0"),
+    "q4": ("decode-b8-kv256k-c65536-q4", dca.attention_q4, oracle.attention_q4, synth.q4_0_blocks, "q4_0"),
+}
+FMTS = list(FORMATS)
 
 
-def _q8_dev(inp):
+def _dev_cache(inp):
     codes = torch.from_numpy(np.ascontiguousarray(inp["k_codes"])).to(dev())
     scales = torch.from_numpy(np.ascontiguousarray(inp["k_scales"]).view(np.int16)).to(dev())
     return codes, scales
 
 
-def _oracle_q8(inp, w, chunk=None, rows=None, remap_mode=0):
-    ff = inp["freq_factors"].astype(np.float64) if w.ff_uniform else None
-    return oracle.attention_q8(inp["q"], inp["q_pos"], inp["k_codes"], inp["k_scales"],
-                               chunk=w.chunk if chunk is None else chunk, n_rot=w.n_rot,
-                               theta=w.theta, scale=w.scale, freq_factors=ff, rows=rows,
-                               per_regime=False, remap_mode=remap_mode)
-
-
-def _run_and_check(inp, w, chunk=None, remap_mode=0, o_dtype=torch.float32, rows=None):
+def _run_and_check(fmt, inp, w, chunk=None, remap_mode=0, o_dtype=torch.float32, rows=None):
+    _, gpu_fn, oracle_fn, _, _ = FORMATS[fmt]
     B, T, Hq, D = inp["q"].shape
     ffd = to_dev(inp["freq_factors"]) if w.ff_uniform else None
     cfg = cfg_for(w, ffd, chunk=chunk, remap_mode=remap_mode)
-    codes, scales = _q8_dev(inp)
-    o, lse = dca.attention_q8(cfg, to_dev(inp["q"]), to_dev(inp["q_pos"]), codes, scales, o_dtype=o_dtype)
+    codes, scales = _dev_cache(inp)
+    o, lse = gpu_fn(cfg, to_dev(inp["q"]), to_dev(inp["q_pos"]), codes, scales, o_dtype=o_dtype)
     torch.cuda.synchronize()
-    res = _oracle_q8(inp, w, chunk=chunk, rows=rows, remap_mode=remap_mode)
+    ff = inp["freq_factors"].astype(np.float64) if w.ff_uniform else None
+    res = oracle_fn(inp["q"], inp["q_pos"], inp["k_codes"], inp["k_scales"],
+                    chunk=w.chunk if chunk is None else chunk, n_rot=w.n_rot, theta=w.theta,
+                    scale=w.scale, freq_factors=ff, rows=rows, per_regime=False, remap_mode=remap_mode)
     sel = res["rows"]
     got_o = o.float().cpu().numpy().reshape(B * T, Hq, D)[sel]
     got_l = lse.cpu().numpy().reshape(B * T, Hq)[sel]
@@ -63,32 +64,37 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("label,over,chunk,mode", CASES, ids=[c[0] for c in CASES])
-def test_q8_decode_cases(label, over, chunk, mode):
-    inp = synth.make_inputs(Q8, **over)
-    res = _run_and_check(inp, inp["w"], chunk=chunk, remap_mode=mode)
+def test_quant_decode_cases(label, over, chunk, mode, fmt):
+    inp = synth.make_inputs(FORMATS[fmt][0], **over)
+    res = _run_and_check(fmt, inp, inp["w"], chunk=chunk, remap_mode=mode)
     if label == "empty-cache":
         assert np.isneginf(res["lse"]).all()
 
 
-def test_q8_decode_full_workload():
-    """The 256k-key, batch-8 decode over the q8_0 cache at its real sizes and chunk, bf16 output as
-    timed; every head of three of the eight rows (the oracle's cost is ~256k keys per row)."""
-    inp = synth.make_inputs(Q8)
-    _run_and_check(inp, inp["w"], o_dtype=torch.bfloat16, rows=np.array([0, 5, 7], np.int64))
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quant_decode_full_workload(fmt):
+    """The 256k-key, batch-8 decode over the quantized cache at its real sizes and chunk, bf16
+    output as timed; every head of three of the eight rows (the oracle's cost is ~256k keys per
+    row)."""
+    inp = synth.make_inputs(FORMATS[fmt][0])
+    _run_and_check(fmt, inp, inp["w"], o_dtype=torch.bfloat16, rows=np.array([0, 5, 7], np.int64))
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("Hq,Hkv", [(2, 2), (4, 2), (8, 2), (16, 1)])
-def test_q8_gqa_ratios(Hq, Hkv):
-    w = synth.Workload("gqa-q8", 2, 2, 3000, 3002, 1024, Hq, Hkv, "q8_0", 79)
-    _run_and_check(synth.make_inputs(w), w)
+def test_quant_gqa_ratios(Hq, Hkv, fmt):
+    w = synth.Workload("gqa-" + fmt, 2, 2, 3000, 3002, 1024, Hq, Hkv, FORMATS[fmt][4], 79)
+    _run_and_check(fmt, synth.make_inputs(w), w)
 
 
-def _needle_inputs(T, N, q0, seed, scale_q=1.0):
+def _needle_inputs(fmt, T, N, q0, seed, scale_q=1.0):
     """Float keys with needles (a few keys set to the unit-RMS direction of a query head's tail),
-    then stored as q8_0: the needles dominate their row's softmax, so |O| ~ 1 and the 1e-2 bar
-    bites.  scale_q > 1 makes the needle scores far exceed everything before them (rescale path)."""
-    w = synth.Workload("needle-q8", 1, T, q0, N, 256 if T > 1 else 1024, 16, 2, "q8_0", seed)
+    then stored in the quantized format: the needles dominate their row's softmax, so |O| ~ 1 and
+    the 1e-2 bar bites.  scale_q > 1 makes the needle scores far exceed everything before them
+    (rescale path)."""
+    w = synth.Workload("needle-" + fmt, 1, T, q0, N, 256 if T > 1 else 1024, 16, 2, FORMATS[fmt][4], seed)
     inp = synth.make_inputs(w)
     rng = np.random.default_rng(seed + 1)
     q = synth.bf16_to_f32(inp["q"]).copy()
@@ -100,28 +106,31 @@ def _needle_inputs(T, N, q0, seed, scale_q=1.0):
             qq = q[0, t, h, 128:]
             k[0, j, h // 8, 128:] = qq / np.sqrt(np.mean(qq ** 2))
     inp["q"] = synth.bf16_bits(q)
-    inp["k_codes"], inp["k_scales"] = synth.q8_0_blocks(k)
+    inp["k_codes"], inp["k_scales"] = FORMATS[fmt][3](k)
     return inp, w
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("T,N,q0,scale_q", [(1, 3000, 2999, 1.0), (4, 5000, 4990, 1.0),
                                              (1, 3000, 2999, 12.0)])
-def test_q8_needles(T, N, q0, scale_q):
-    inp, w = _needle_inputs(T, N, q0, 41 + T, scale_q)
-    res = _run_and_check(inp, w)
+def test_quant_needles(T, N, q0, scale_q, fmt):
+    inp, w = _needle_inputs(fmt, T, N, q0, 41 + T, scale_q)
+    res = _run_and_check(fmt, inp, w)
     assert np.abs(res["o"]).max() > 0.3
     if scale_q > 1:
         assert res["lse"].max() > 100.0
 
 
-def test_q8_bitwise_deterministic():
-    inp = synth.make_inputs(Q8, B=2, N=50000, q0=49999)
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quant_bitwise_deterministic(fmt):
+    inp = synth.make_inputs(FORMATS[fmt][0], B=2, N=50000, q0=49999)
     w = inp["w"]
     cfg = cfg_for(w, to_dev(inp["freq_factors"]), chunk=8192)
-    codes, scales = _q8_dev(inp)
+    codes, scales = _dev_cache(inp)
     q, qp = to_dev(inp["q"]), to_dev(inp["q_pos"])
-    o1, l1 = dca.attention_q8(cfg, q, qp, codes, scales)
-    o2, l2 = dca.attention_q8(cfg, q, qp, codes, scales)
+    gpu_fn = FORMATS[fmt][1]
+    o1, l1 = gpu_fn(cfg, q, qp, codes, scales)
+    o2, l2 = gpu_fn(cfg, q, qp, codes, scales)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(l1, l2)

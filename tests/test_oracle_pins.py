@@ -527,3 +527,63 @@ def test_attention_q8_equals_attention_over_the_dequantized_cache(mode):
     assert np.abs(kf - kx).max() <= np.abs(kx).max() / 127 / 2 * 1.01
     raw = oracle.attention(synth.bf16_to_f32(inp["q"]), inp["q_pos"], kx, **kw)
     assert 0 < np.abs(raw["lse"] - res["lse"]).max() < 0.05
+
+
+def test_dequant_q4_hand_example():
+    """One row of two q4_0 blocks worked by hand: dim 2j in the low nibble of byte j.  Block 0 has
+    d = 0.5 (0x3800): byte 0 = 0xF0 gives dims 0, 1 = (0 - 8, 15 - 8) * 0.5 = (-4, 3.5); byte 1 =
+    0x98 gives (8 - 8, 9 - 8) * 0.5 = (0, 0.5).  Block 1 has d = -2 (0xC000): byte 16 = 0x1E gives
+    dims 32, 33 = (14 - 8, 1 - 8) * -2 = (-12, 14)."""
+    codes = np.full((1, 32), 0x88, np.uint8)       # every other dim: code 8, value 0
+    codes[0, 0], codes[0, 1], codes[0, 16] = 0xF0, 0x98, 0x1E
+    scales = np.array([[0x3800, 0xC000]], np.uint16)
+    want = np.zeros((1, 64))
+    want[0, :4] = [-4.0, 3.5, 0.0, 0.5]
+    want[0, 32:34] = [-12.0, 14.0]
+    assert np.array_equal(oracle.dequant_q4(codes, scales), want)
+
+
+def test_q4_quantizer_round_trip_bound():
+    """The synthetic q4_0 store: codes in [1, 15], every nonzero block reaches |n - 8| = 7, an
+    all-zero block stores code 8, and d*(n - 8) is within half a step (plus the fp16 rounding of
+    d) of the drawn value."""
+    x = np.random.default_rng(13).standard_normal((40, 2, 64)).astype(np.float32) * 3
+    x[0, 0, :32] = 0.0
+    codes, scales = synth.q4_0_blocks(x)
+    assert codes.shape == (40, 2, 32) and scales.shape == (40, 2, 2)
+    n = np.stack([codes & 15, codes >> 4], axis=-1).reshape(40, 2, 64).astype(np.int64)
+    assert n.min() >= 0 and n.max() <= 15
+    dev_ = np.abs(n - 8).reshape(40, 2, 2, 32).max(axis=-1)
+    nonzero = np.abs(x.reshape(40, 2, 2, 32)).max(axis=-1) > 0
+    assert (dev_[nonzero] == 7).all() and (dev_[~nonzero] == 0).all()
+    d_exact = np.abs(x.reshape(40, 2, 2, 32)).max(axis=-1).astype(np.float64) / 7
+    d_store = scales.view(np.float16).astype(np.float64)
+    err = np.abs(oracle.dequant_q4(codes, scales).reshape(40, 2, 2, 32) - x.reshape(40, 2, 2, 32))
+    bound = d_exact / 2 * (1 + 1e-6) + np.abs(d_store - d_exact) * 7 + 1e-30
+    assert (err <= bound[..., None]).all()
+
+
+def test_q4_generator_is_deterministic_and_blocks_agree():
+    shape = (2, 40, 2, 64)
+    c1, s1 = synth._normal_q4(np.random.default_rng(5), shape, chunk_elems=1 << 10)
+    c2, s2 = synth._normal_q4(np.random.default_rng(5), shape, chunk_elems=1 << 14)
+    x = np.random.default_rng(5).standard_normal(int(np.prod(shape)), dtype=np.float32).reshape(shape)
+    c3, s3 = synth.q4_0_blocks(x)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+    assert np.array_equal(c1, c3) and np.array_equal(s1, s3)
+
+
+@pytest.mark.parametrize("mode", [oracle.REMAP_BASELINE, oracle.REMAP_PAGE_2C])
+def test_attention_q4_equals_attention_over_the_dequantized_cache(mode):
+    """d * (n - 8) (11-bit times 4-bit significand) is exact in float32, so attention over the q4_0
+    cache must equal, to the last bit, attention over the float32 cache of those values."""
+    w = synth.Workload("t4", 2, 7, 30, 37, 8, 4, 2, "q4_0", 22, D=64, n_rot=16)
+    inp = synth.make_inputs(w)
+    ff = inp["freq_factors"].astype(np.float64)
+    kw = dict(chunk=w.chunk, n_rot=w.n_rot, theta=w.theta, scale=0.125, freq_factors=ff, remap_mode=mode)
+    res = oracle.attention_q4(inp["q"], inp["q_pos"], inp["k_codes"], inp["k_scales"], **kw)
+    kf = oracle.dequant_q4(inp["k_codes"], inp["k_scales"])
+    assert np.array_equal(kf.astype(np.float32).astype(np.float64), kf)
+    ref = oracle.attention(synth.bf16_to_f32(inp["q"]), inp["q_pos"], kf.astype(np.float32), **kw)
+    for key in ("o", "lse", "o_reg", "lse_reg"):
+        assert np.array_equal(res[key], ref[key]), key
