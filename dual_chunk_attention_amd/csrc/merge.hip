@@ -59,8 +59,9 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   if (a.lse_out && lane == 0) a.lse_out[row] = M + logf(W);
 }
 
-// Many parts per row (split-KV partials): one workgroup per row.  Non-empty parts are compacted
-// in index order, split over the 4 waves, and the wave sums are added in a fixed order.
+// Many parts per row (split-KV partials): one workgroup per (row, slice of 256 dims).  Non-empty
+// parts are compacted in index order, split over the 4 waves (lane: 4 dims, 16-byte loads, four
+// parts in flight), and the wave sums are added in a fixed order.
 constexpr int kMaxManyParts = 2048;
 
 template <typename OutT>
@@ -68,7 +69,7 @@ __global__ __launch_bounds__(256) void merge_many_kernel(MergeArgs a) {
   __shared__ float s_l[kMaxManyParts];
   __shared__ float s_w[kMaxManyParts];
   __shared__ int s_idx[kMaxManyParts];
-  __shared__ float s_acc[3][1024];
+  __shared__ float s_acc[3][256];
   __shared__ float s_M, s_W;
   __shared__ int s_cnt;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -105,40 +106,47 @@ __global__ __launch_bounds__(256) void merge_many_kernel(MergeArgs a) {
   __syncthreads();
   const int cnt = s_cnt;
   OutT* out = (OutT*)a.o_out + row * a.D;
+  const int d = blockIdx.y * 256 + 4 * lane;   // the lane's 4 dims (D is a multiple of 4)
+  const bool live = d < a.D;
   if (cnt == 0) {
-    for (int d = tid; d < a.D; d += 256) out[d] = from_f32<OutT>(0.0f);
-    if (a.lse_out && tid == 0) a.lse_out[row] = -INFINITY;
+    if (wv == 0 && live) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) out[d + k] = from_f32<OutT>(0.0f);
+    }
+    if (a.lse_out && blockIdx.y == 0 && tid == 0) a.lse_out[row] = -INFINITY;
     return;
   }
-  float acc[16];
+  f32x4 acc = f32x4{};
+  if (live) {
+    int e = wv;
+    for (; e + 12 < cnt; e += 16) {
+      f32x4 v[4];
 #pragma unroll
-  for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
-  for (int e = wv; e < cnt; e += 4) {
-    const float wgt = s_w[e];
-    const float* o = part_o(a, s_idx[e], row);
+      for (int k = 0; k < 4; ++k) v[k] = *(const f32x4*)(part_o(a, s_idx[e + 4 * k], row) + d);
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int d = lane + 64 * k;
-      if (d < a.D) acc[k] = fmaf(wgt, o[d], acc[k]);
+      for (int k = 0; k < 4; ++k) {
+        const float wgt = s_w[e + 4 * k];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] = fmaf(wgt, v[k][c], acc[c]);
+      }
+    }
+    for (; e < cnt; e += 4) {
+      const f32x4 v = *(const f32x4*)(part_o(a, s_idx[e], row) + d);
+      const float wgt = s_w[e];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] = fmaf(wgt, v[c], acc[c]);
     }
   }
-  if (wv > 0) {
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int d = lane + 64 * k;
-      if (d < a.D) s_acc[wv - 1][d] = acc[k];
-    }
-  }
+  if (wv > 0 && live) *(f32x4*)&s_acc[wv - 1][4 * lane] = acc;
   __syncthreads();
-  if (wv == 0) {
+  if (wv == 0 && live) {
     const float inv = 1.0f / s_W;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int d = lane + 64 * k;
-      if (d < a.D) out[d] = from_f32<OutT>((((acc[k] + s_acc[0][d]) + s_acc[1][d]) + s_acc[2][d]) * inv);
-    }
-    if (a.lse_out && lane == 0) a.lse_out[row] = s_M + logf(s_W);
+    for (int c = 0; c < 4; ++c)
+      out[d + c] = from_f32<OutT>((((acc[c] + s_acc[0][4 * lane + c]) + s_acc[1][4 * lane + c]) +
+                                   s_acc[2][4 * lane + c]) * inv);
   }
+  if (a.lse_out && blockIdx.y == 0 && tid == 0) a.lse_out[row] = s_M + logf(s_W);
 }
 
 }  // namespace
@@ -147,11 +155,12 @@ int merge_many_max_parts() { return kMaxManyParts; }
 
 hipError_t launch_merge_many(const MergeArgs& a, bool out_bf16, hipStream_t stream) {
   if (a.rows <= 0) return hipSuccess;
-  if (a.n_parts > kMaxManyParts || a.D > 1024) return hipErrorInvalidValue;
+  if (a.n_parts > kMaxManyParts || a.D > 1024 || a.D % 4) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)a.rows, (unsigned)((a.D + 255) / 256));
   if (out_bf16)
-    hipLaunchKernelGGL(merge_many_kernel<bf16>, dim3((unsigned)a.rows), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(merge_many_kernel<bf16>, grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(merge_many_kernel<float>, dim3((unsigned)a.rows), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(merge_many_kernel<float>, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
