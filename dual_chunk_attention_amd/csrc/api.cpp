@@ -95,7 +95,7 @@ struct AttnWorkspace {
 };
 
 AttnWorkspace attention_layout(const dca_config* cfg, dca_dtype dtype, int32_t B, int32_t T,
-                               int32_t n_kv, bool split_kv = false) {
+                               int32_t n_kv, bool split_kv = false, int32_t n_spans_override = 0) {
   AttnWorkspace w{};
   const size_t rows = (size_t)B * T;
   const size_t es = elem_size(dtype);
@@ -113,6 +113,7 @@ AttnWorkspace attention_layout(const dca_config* cfg, dca_dtype dtype, int32_t B
   w.krot = take(dec ? 0 : (size_t)B * n_kv * Hkv * R * es);
   if (dec) {
     decode_split(n_kv, &w.span, &w.n_spans);
+    if (n_spans_override > 0) w.n_spans = n_spans_override;
     w.n_hi = (cfg->chunk + 63) / 64;
     w.o_parts = take(0);
     w.lse_parts = take(0);
@@ -167,6 +168,39 @@ dca::RopeArgs rope_args_for_q(const dca_config* cfg, const void* q, int64_t rows
   ra.theta = (double)cfg->rope_theta;
   ra.freq_factors = cfg->freq_factors;
   return ra;
+}
+
+// Spans of the window / tail decode: each region is cut into spans of the whole cache's span size.
+void window_spans(int32_t n_win, int32_t n_tail, int32_t* span, int32_t* s_win, int32_t* s_tail) {
+  int32_t n_spans;
+  decode_split(n_win + n_tail, span, &n_spans);
+  *s_win = (int32_t)(((int64_t)n_win + *span - 1) / *span);
+  *s_tail = (int32_t)(((int64_t)n_tail + *span - 1) / *span);
+}
+
+// Address at which the kernels read caller memory: device memory as it is, pinned host memory
+// (hipHostMalloc) at the device address the runtime maps it to.  Pageable host memory or an
+// unknown pointer is rejected before any launch.
+dca_status device_view(const void* p, const void** out, const char* what) {
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(DCA_ERR_INVALID_ARGUMENT, "%s: not device or pinned host memory", what);
+  }
+  if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged) {
+    *out = p;
+    return DCA_OK;
+  }
+  if (at.type == hipMemoryTypeHost) {
+    void* d = nullptr;
+    if (hipHostGetDevicePointer(&d, const_cast<void*>(p), 0) != hipSuccess || !d) {
+      (void)hipGetLastError();
+      return fail(DCA_ERR_INVALID_ARGUMENT, "%s: host memory not mapped for the device", what);
+    }
+    *out = d;
+    return DCA_OK;
+  }
+  return fail(DCA_ERR_INVALID_ARGUMENT, "%s: unsupported memory type %d", what, (int)at.type);
 }
 
 }  // namespace
@@ -278,6 +312,8 @@ dca_status dca_attn_regime(const dca_config* cfg, dca_dtype dtype, int32_t regim
   da.lse_part = (float*)((char*)workspace + align_up((size_t)da.n_spans * prow * cfg->head_dim * 4));
   da.regime_mask = 1 << regime;  // its partials fill slots [0, n_spans)
   da.chunk = cfg->chunk;
+  da.key0 = 0;
+  da.n_rows = n_kv;
   st = hip_status(dca::launch_attn_decode_bf16(da, stream), "decode attention launch");
   if (st) return st;
   dca::MergeArgs m{};
@@ -384,6 +420,8 @@ dca_status dca_attention(const dca_config* cfg, dca_dtype dtype, int32_t B, int3
     da.rot_lo = lo;
     da.rot_hi = hi;
     da.chunk = cfg->chunk;
+    da.key0 = 0;
+    da.n_rows = n_kv;
     if ((st = hip_status(dca::launch_attn_decode_bf16(da, stream), "decode attention launch")))
       return st;
     if ((st = hip_status(mark(4, stream), "stage event"))) return st;
@@ -526,6 +564,8 @@ static dca_status attention_quant(int bits, const dca_config* cfg, int32_t B, in
   da.rot_lo = lo;
   da.rot_hi = hi;
   da.chunk = cfg->chunk;
+  da.key0 = 0;
+  da.n_rows = n_kv;
   if ((st = hip_status(bits == 8 ? dca::launch_attn_decode_q8(da, stream) : dca::launch_attn_decode_q4(da, stream),
                        "quantized decode attention launch")))
     return st;
@@ -587,6 +627,129 @@ dca_status dca_probe_hbm_read(const void* src, int64_t bytes, int32_t n_workgrou
   if (n_workgroups < 1 || n_workgroups > 65536)
     return fail(DCA_ERR_INVALID_ARGUMENT, "n_workgroups %d out of range", n_workgroups);
   return hip_status(dca::launch_probe_read(src, bytes, n_workgroups, sink, stream), "probe launch");
+}
+
+
+size_t dca_attention_window_workspace_size(const dca_config* cfg, int32_t B, int32_t T, int32_t n_win,
+                                           int32_t n_tail) {
+  if (check_config(cfg, DCA_BF16) || check_sizes(B, T, n_win) || check_sizes(B, T, n_tail)) return 0;
+  int32_t span, sw, st;
+  window_spans(n_win, n_tail, &span, &sw, &st);
+  return attention_layout(cfg, DCA_BF16, B, T, n_win + n_tail, true, sw + st).total;
+}
+
+dca_status dca_attention_window(const dca_config* cfg, int32_t B, int32_t T, const void* q,
+                                const int32_t* q_pos, const dca_kv_region* window,
+                                const dca_kv_region* tail, dca_dtype o_dtype, void* o, float* lse,
+                                void* workspace, size_t ws_bytes, hipStream_t stream) {
+  dca_status st = check_config(cfg, DCA_BF16);
+  if (st) return st;
+  if (!window || !tail) return fail(DCA_ERR_INVALID_ARGUMENT, "region descriptor is NULL");
+  const dca_kv_region* reg[2] = {window, tail};
+  for (int i = 0; i < 2; ++i) {
+    if (reg[i]->n < 0) return fail(DCA_ERR_INVALID_ARGUMENT, "negative region size %d", reg[i]->n);
+    if (reg[i]->format < DCA_KV_BF16 || reg[i]->format > DCA_KV_Q4_0)
+      return fail(DCA_ERR_INVALID_ARGUMENT, "unknown key format %d", (int)reg[i]->format);
+  }
+  if ((int64_t)window->n + tail->n > INT32_MAX) return fail(DCA_ERR_INVALID_ARGUMENT, "cache too long");
+  const int32_t n_kv = window->n + tail->n;
+  if ((st = check_sizes(B, T, n_kv))) return st;
+  if (!valid_dtype(o_dtype)) return fail(DCA_ERR_INVALID_ARGUMENT, "unknown o_dtype %d", (int)o_dtype);
+  const int64_t rows = (int64_t)B * T;
+  if (rows == 0) return DCA_OK;
+  if (!q || !q_pos || !o) return fail(DCA_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (rows * cfg->n_head_kv > 65535) return fail(DCA_ERR_UNSUPPORTED, "batch too large for the split-KV path");
+  for (int i = 0; i < 2; ++i)
+    if (reg[i]->n > 0 && (!reg[i]->keys || (reg[i]->format != DCA_KV_BF16 && !reg[i]->scales)))
+      return fail(DCA_ERR_INVALID_ARGUMENT, "NULL pointer in the %s region", i ? "tail" : "window");
+  int32_t span, s_win, s_tail;
+  window_spans(window->n, tail->n, &span, &s_win, &s_tail);
+  const int32_t s_all = s_win + s_tail;
+  const AttnWorkspace L = attention_layout(cfg, DCA_BF16, B, T, n_kv, true, s_all);
+  if (ws_bytes < L.total || !workspace)
+    return fail(DCA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", ws_bytes, L.total);
+  const void* keys[2] = {nullptr, nullptr};
+  const void* scales[2] = {nullptr, nullptr};
+  for (int i = 0; i < 2; ++i) {
+    if (reg[i]->n == 0) continue;
+    if ((st = device_view(reg[i]->keys, &keys[i], i ? "tail keys" : "window keys"))) return st;
+    if (reg[i]->format != DCA_KV_BF16 &&
+        (st = device_view(reg[i]->scales, &scales[i], i ? "tail scales" : "window scales")))
+      return st;
+  }
+  char* ws = (char*)workspace;
+  int32_t* pos_q = (int32_t*)(ws + L.pos_q);
+  int32_t* bounds = (int32_t*)(ws + L.bounds);
+  void* qrot = ws + L.qrot;
+  const int64_t Hq = cfg->n_head_q, R = cfg->n_rot, D = cfg->head_dim;
+
+  if ((st = hip_status(mark(0, stream), "stage event"))) return st;
+  if ((st = hip_status(dca::launch_remap(q_pos, rows, cfg->chunk, cfg->remap_mode, n_kv, pos_q, nullptr, bounds, stream),
+                       "remap launch")))
+    return st;
+  if ((st = hip_status(mark(1, stream), "stage event"))) return st;
+  dca::RopeArgs rq = rope_args_for_q(cfg, q, rows, qrot, pos_q);
+  if ((st = hip_status(dca::launch_rope(rq, true, stream), "rope(q) launch"))) return st;
+  if ((st = hip_status(mark(2, stream), "stage event"))) return st;
+  float2* lo = (float2*)(ws + L.tab_lo);
+  float2* hi = (float2*)(ws + L.tab_hi);
+  if ((st = hip_status(dca::launch_rope_tables(lo, hi, L.n_hi, cfg->n_rot, (double)cfg->rope_theta,
+                                               cfg->freq_factors, stream), "rope tables launch")))
+    return st;
+  if ((st = hip_status(mark(3, stream), "stage event"))) return st;
+
+  dca::DecodeArgs da{};
+  dca::AttnArgs& a = da.base;
+  for (int r = 0; r < 3; ++r) a.q_rot[r] = (const char*)qrot + (size_t)r * rows * Hq * R * 2;
+  a.q_rot_hs = R;
+  a.q_tail = (const char*)q + R * 2;
+  a.q_tail_hs = D;
+  a.bounds = bounds;
+  a.B = B; a.T = T; a.Hq = cfg->n_head_q; a.Hkv = cfg->n_head_kv; a.n_kv = n_kv;
+  a.D = cfg->head_dim; a.n_rot = cfg->n_rot; a.scale = cfg->scale;
+  a.rot_f16 = 1;
+  da.o_part = (float*)(ws + L.dec_o);
+  da.lse_part = (float*)(ws + L.dec_lse);
+  da.span = span;
+  da.regime_mask = 7;
+  da.rot_lo = lo;
+  da.rot_hi = hi;
+  da.chunk = cfg->chunk;
+  // the tail first (read over the host link when it lives in host memory), then the window; the
+  // spans of region i take partial slots [r * s_all + first_span, ...) of regime r
+  const int order[2] = {1, 0};
+  for (int oi = 0; oi < 2; ++oi) {
+    const int i = order[oi];
+    if (reg[i]->n == 0) continue;
+    a.k_raw = keys[i];
+    da.k_scales = (const uint16_t*)scales[i];
+    da.key0 = i ? window->n : 0;
+    da.n_rows = reg[i]->n;
+    da.n_spans = i ? s_tail : s_win;
+    for (int r = 0; r < 3; ++r) da.slot0[r] = r * s_all + (i ? s_win : 0);
+    hipError_t e;
+    switch (reg[i]->format) {
+      case DCA_KV_BF16: e = dca::launch_attn_decode_bf16(da, stream); break;
+      case DCA_KV_Q8_0: e = dca::launch_attn_decode_q8(da, stream); break;
+      default: e = dca::launch_attn_decode_q4(da, stream); break;
+    }
+    if ((st = hip_status(e, "region decode attention launch"))) return st;
+  }
+  if ((st = hip_status(mark(4, stream), "stage event"))) return st;
+  dca::MergeArgs m{};
+  m.o_base = da.o_part;
+  m.lse_base = da.lse_part;
+  m.o_part_stride = rows * Hq * D;
+  m.lse_part_stride = rows * Hq;
+  m.n_parts = 3 * s_all;
+  m.strided = 1;
+  m.rows = rows * Hq;
+  m.D = cfg->head_dim;
+  m.o_out = o;
+  m.lse_out = lse;
+  if ((st = hip_status(dca::launch_merge_many(m, o_dtype == DCA_BF16, stream), "split merge launch")))
+    return st;
+  return hip_status(mark(5, stream), "stage event");
 }
 
 }  // extern "C"

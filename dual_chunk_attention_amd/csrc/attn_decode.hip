@@ -64,14 +64,16 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(DecodeArgs da) {
   const int g = (int)(btg % a.Hkv);
   const int64_t bt = btg / a.Hkv;
   const int b = (int)(bt / a.T);
-  const int span_lo = span * da.span;
-  const int span_hi = min(span_lo + da.span, a.n_kv) - 1;
+  const int key_end = da.key0 + da.n_rows;   // one past the region's last cell
+  const int span_lo = da.key0 + span * da.span;
+  const int span_hi = min(span_lo + da.span, key_end) - 1;
   const bool head_ok = hcol < G;
   const int64_t rowhead = bt * a.Hq + (int64_t)g * G + (head_ok ? hcol : 0);
 
-  const bf16* kraw_b = (const bf16*)a.k_raw + ((int64_t)b * a.n_kv * a.Hkv + g) * kD;
+  // rows of the region: cell j at row j - key0
+  const bf16* kraw_b = (const bf16*)a.k_raw + ((int64_t)b * da.n_rows * a.Hkv + g) * kD;
   const bf16* krot_b =
-      ROTATE ? nullptr : (const bf16*)a.k_rot + ((int64_t)b * a.n_kv * a.Hkv + g) * a.k_rot_hs;
+      ROTATE ? nullptr : (const bf16*)a.k_rot + ((int64_t)b * da.n_rows * a.Hkv + g) * a.k_rot_hs;
   const int half_rot = a.n_rot / 2;   // 64
   const float scale_log2 = a.scale * kLog2e;
 
@@ -135,17 +137,16 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(DecodeArgs da) {
 
     const int kt0 = lo / kTile, kt1 = hi / kTile;
     // tile k0..k0+63 by direct global->LDS loads: wave w fills rows 16w..16w+15, lane l the
-    // physical chunk l of a row with logical chunk l ^ swz(row); rows past the cache re-read its
-    // last key (their scores are masked)
+    // physical chunk l of a row with logical chunk l ^ swz(row); rows outside the region re-read
+    // its first or last cell (their scores are masked)
     auto issue = [&](int buf, int k0) {
       const uint32_t base = kbuf_lds + buf * kTileBytes;
       const int64_t key_bytes = (int64_t)a.Hkv * kD * 2;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int row = 16 * wu + i;
-        int key = k0 + row;
-        key = min(max(key, 0), a.n_kv - 1);
-        const char* src = uniform_ptr((const char*)kraw_b + (int64_t)key * key_bytes);
+        const int key = min(max(k0 + row, da.key0), key_end - 1);
+        const char* src = uniform_ptr((const char*)kraw_b + (int64_t)(key - da.key0) * key_bytes);
         dma16(src + 16 * (l ^ swz(row)), base + row * 1024);
       }
       if (tab_tile && wu == 0) {   // hi row of the tile (lanes 32..63 fetch the next row, unused)
@@ -202,7 +203,8 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(DecodeArgs da) {
           rotate([&](int, int f) { return tlo[f]; }, [&](int f) { return thi[f]; });
         }
       } else {
-        const bf16* kr = krot_b + (int64_t)min(key, a.n_kv - 1) * a.Hkv * a.k_rot_hs + 8 * gq;  // 2-byte elements
+        const int krow = min(max(key, da.key0), key_end - 1) - da.key0;
+        const bf16* kr = krot_b + (int64_t)krow * a.Hkv * a.k_rot_hs + 8 * gq;  // 2-byte elements
 #pragma unroll
         for (int s = 0; s < 4; ++s) kf[s] = *(const bf16x8*)(kr + 32 * s);
       }

@@ -152,13 +152,15 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
   const int g = (int)(btg % a.Hkv);
   const int64_t bt = btg / a.Hkv;
   const int b = (int)(bt / a.T);
-  const int span_lo = span * da.span;
-  const int span_hi = min(span_lo + da.span, a.n_kv) - 1;
+  const int key_end = da.key0 + da.n_rows;   // one past the region's last cell
+  const int span_lo = da.key0 + span * da.span;
+  const int span_hi = min(span_lo + da.span, key_end) - 1;
   const bool head_ok = hcol < G;
   const int64_t rowhead = bt * a.Hq + (int64_t)g * G + (head_ok ? hcol : 0);
 
-  const char* codes_b = (const char*)a.k_raw + ((int64_t)b * a.n_kv * a.Hkv + g) * kRow;
-  const uint16_t* scales_b = da.k_scales + ((int64_t)b * a.n_kv * a.Hkv + g) * (kD / 32);
+  // rows of the region: cell j at row j - key0
+  const char* codes_b = (const char*)a.k_raw + ((int64_t)b * da.n_rows * a.Hkv + g) * kRow;
+  const uint16_t* scales_b = da.k_scales + ((int64_t)b * da.n_rows * a.Hkv + g) * (kD / 32);
   const int half_rot = a.n_rot / 2;   // 64
   const float scale_log2 = a.scale * kLog2e;
 
@@ -224,20 +226,21 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
     // tile k0..k0+63 by direct global->LDS loads into stage buf: wave w the code rows
     // 16w..16w+15 (kRpl rows of kRow bytes per load; position p of row r receives global chunk
     // p ^ (r & 15)), waves 0 and 1 the scale rows 0..31 and 32..63 (lane l the half l%2 of row
-    // l/2), lanes 0..31 of wave 2 the hi table row; rows past the cache re-read its last key
-    // (their scores are masked)
+    // l/2), lanes 0..31 of wave 2 the hi table row; rows outside the region re-read its first or
+    // last cell (their scores are masked)
     auto issue = [&](int buf, int k0) {
       const uint32_t base = stage_lds + buf * kStageBytes;
       const int ln = opaque(l);
-      const int last = a.n_kv - 1 - k0;   // the tile's last row inside the cache
+      // tile row r reads region row k0 - key0 + r, clamped to the region: r in [first, last]
+      const int first = max(da.key0 - k0, 0), last = key_end - 1 - k0;
       const uint32_t key_bytes = (uint32_t)a.Hkv * kRow, key_sbytes = (uint32_t)a.Hkv * (kD / 32) * 2;
-      const char* cb = uniform_ptr(codes_b + (int64_t)k0 * key_bytes);
+      const char* cb = uniform_ptr(codes_b + (int64_t)(k0 - da.key0) * key_bytes);
       // row 16 wu + kRpl i + hb (hb = the lane's row within the load) has swizzle key
       // kRpl i + hb = kRpl i ^ hb, so the lane's chunk offset is x ^ 16 kRpl i
       constexpr int kLanesPerRow = 64 / kRpl;
       const int hb = ln / kLanesPerRow;
       const uint32_t x = 16 * ((ln % kLanesPerRow) ^ hb);
-      if (last >= kTile - 1) {   // whole tile inside the cache: row offsets step by kRpl keys
+      if (first == 0 && last >= kTile - 1) {   // whole tile inside the region: rows step by kRpl keys
         const uint32_t r0 = __umul24((uint32_t)(16 * wu + hb), key_bytes);
 #pragma unroll
         for (int i = 0; i < 16 / kRpl; ++i)
@@ -246,14 +249,15 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
 #pragma unroll
         for (int i = 0; i < 16 / kRpl; ++i) {
           const int row = 16 * wu + kRpl * i + hb;
-          dma16_off(cb, __umul24((uint32_t)min(row, last), key_bytes) + (x ^ (16 * kRpl * i)),
+          dma16_off(cb, __umul24((uint32_t)min(max(row, first), last), key_bytes) + (x ^ (16 * kRpl * i)),
                     base + (16 * wu + kRpl * i) * kRow);
         }
       }
       if (wu < 2) {
         const int row = 32 * wu + (ln >> 1);
-        const char* sb = uniform_ptr((const char*)scales_b + (int64_t)k0 * key_sbytes);
-        dma16_off(sb, __umul24((uint32_t)min(row, last), key_sbytes) + 16 * (ln & 1), base + kCodeBytes + wu * 1024);
+        const char* sb = uniform_ptr((const char*)scales_b + (int64_t)(k0 - da.key0) * key_sbytes);
+        dma16_off(sb, __umul24((uint32_t)min(max(row, first), last), key_sbytes) + 16 * (ln & 1),
+                  base + kCodeBytes + wu * 1024);
       }
       if (tab_tile && wu == 2 && ln < 32) {   // hi row of the tile (512 bytes: lanes 0..31)
         const int hr = (int)((int64_t)k0 % da.chunk >> 6);

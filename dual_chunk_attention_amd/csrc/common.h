@@ -182,6 +182,10 @@ struct DecodeArgs {
   // quantized key cache: base.k_raw holds the codes (q8_0: int8 [B,N,Hkv,D]; q4_0: uint8
   // [B,N,Hkv,D/2], two 4-bit codes per byte) and k_scales the fp16 block scales [B,N,Hkv,D/32]
   const uint16_t* k_scales;
+  // region of the cache this launch reads: k_raw (k_rot, k_scales) hold cells
+  // [key0, key0 + n_rows) of every sequence (N = n_rows above); spans start at key0.  A whole
+  // cache is key0 = 0, n_rows = base.n_kv.
+  int32_t key0, n_rows;
 };
 hipError_t launch_attn_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_attn_decode_q8(const DecodeArgs& a, hipStream_t stream);

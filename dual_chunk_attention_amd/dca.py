@@ -19,6 +19,7 @@ OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = ra
 F32, BF16 = 0, 1
 INTRA, SUCC, INTER = 0, 1, 2
 REMAP_BASELINE, REMAP_PAGE_C, REMAP_PAGE_2C = 0, 1, 2   # dca_remap_mode
+KV_BF16, KV_Q8_0, KV_Q4_0 = 0, 1, 2                    # dca_kv_format
 MAX_MERGE_PARTS = 8
 
 
@@ -34,6 +35,11 @@ class _Config(ctypes.Structure):
                 ("chunk", ctypes.c_int32), ("remap_mode", ctypes.c_int32),
                 ("rope_theta", ctypes.c_float), ("scale", ctypes.c_float),
                 ("freq_factors", ctypes.c_void_p)]
+
+
+class _Region(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int), ("keys", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("n", ctypes.c_int32)]
 
 
 _lib = None
@@ -67,13 +73,19 @@ def lib():
         L.dca_attention_q4.argtypes = L.dca_attention_q8.argtypes
         L.dca_attention_q4_workspace_size.argtypes = [cfgp, i32, i32, i32]
         L.dca_attention_q4_workspace_size.restype = sz
+        regp = ctypes.POINTER(_Region)
+        L.dca_attention_window.argtypes = [cfgp, i32, i32, vp, vp, regp, regp, ctypes.c_int, vp, vp,
+                                           vp, sz, vp]
+        L.dca_attention_window_workspace_size.argtypes = [cfgp, i32, i32, i32, i32]
+        L.dca_attention_window_workspace_size.restype = sz
         L.dca_set_stage_events.argtypes = [vp, i32]
         L.dca_set_stage_events.restype = ctypes.c_int
         L.dca_last_error.restype = ctypes.c_char_p
         L.dca_probe_mfma_bf16.argtypes = [i32, i32, vp, vp]
         L.dca_probe_hbm_read.argtypes = [vp, i64, i32, vp, vp]
         for f in ("dca_remap_positions", "dca_rope_partial", "dca_attn_regime", "dca_lse_merge",
-                  "dca_attention", "dca_attention_q8", "dca_attention_q4", "dca_probe_mfma_bf16", "dca_probe_hbm_read"):
+                  "dca_attention", "dca_attention_q8", "dca_attention_q4", "dca_attention_window",
+                  "dca_probe_mfma_bf16", "dca_probe_hbm_read"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -271,6 +283,56 @@ def attention_q4(cfg: Config, q: torch.Tensor, q_pos: torch.Tensor, k_codes: tor
     L = lib()
     return _attention_quant(L.dca_attention_q4, L.dca_attention_q4_workspace_size, 2, (torch.uint8,),
                             cfg, q, q_pos, k_codes, k_scales, o_dtype, workspace, out, lse)
+
+
+@dataclass
+class Region:
+    """One region of a key cache for attention_window: format KV_BF16 (keys bf16 [B,n,Hkv,D]),
+    KV_Q8_0 (int8 codes [B,n,Hkv,D] + fp16/int16 scales [B,n,Hkv,D/32]) or KV_Q4_0 (uint8 codes
+    [B,n,Hkv,D/2] + scales).  The tensors may live on the GPU or in pinned host memory
+    (torch's pin_memory=True)."""
+    format: int
+    keys: Optional[torch.Tensor]
+    scales: Optional[torch.Tensor] = None
+
+    def n(self) -> int:
+        return 0 if self.keys is None else int(self.keys.shape[1])
+
+    def c(self):
+        if self.keys is not None:
+            assert self.keys.is_contiguous() and (self.scales is None or self.scales.is_contiguous())
+        return _Region(self.format, None if self.keys is None else self.keys.data_ptr(),
+                       None if self.scales is None else self.scales.data_ptr(), self.n())
+
+
+def attention_window_workspace_size(cfg: Config, B: int, T: int, n_win: int, n_tail: int) -> int:
+    c = cfg.c()
+    return int(lib().dca_attention_window_workspace_size(ctypes.byref(c), B, T, n_win, n_tail))
+
+
+def attention_window(cfg: Config, q: torch.Tensor, q_pos: torch.Tensor, window: Region, tail: Region,
+                     o_dtype: Optional[torch.dtype] = None, workspace: Optional[torch.Tensor] = None,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """dca_attention_window: q bf16 [B,T,Hq,D] on the GPU, q_pos int32 [B,T]; cells
+    [0, window.n) of the cache from `window`, [window.n, window.n + tail.n) from `tail` ->
+    (o [B,T,Hq,D] of o_dtype (default bf16), lse fp32 [B,T,Hq])."""
+    B, T, Hq, D = q.shape
+    assert q.dtype == torch.bfloat16 and q_pos.dtype == torch.int32
+    assert q.is_contiguous() and q_pos.is_contiguous()
+    od = o_dtype or torch.bfloat16
+    c = cfg.c()
+    ws_bytes = lib().dca_attention_window_workspace_size(ctypes.byref(c), B, T, window.n(), tail.n())
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, T, Hq, D), dtype=od, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device)
+    rw, rt = window.c(), tail.c()
+    _check(lib().dca_attention_window(ctypes.byref(c), B, T, _ptr(q), _ptr(q_pos), ctypes.byref(rw),
+                                      ctypes.byref(rt), _dtype_code(od), _ptr(out), _ptr(lse),
+                                      _ptr(workspace), workspace.numel(), _stream()))
+    return out, lse
 
 
 N_STAGE_EVENTS = 6

@@ -206,6 +206,42 @@ dca_status dca_attention_q4(const dca_config* cfg, int32_t B, int32_t T, const v
                             size_t ws_bytes, hipStream_t stream);
 size_t dca_attention_q4_workspace_size(const dca_config* cfg, int32_t B, int32_t T, int32_t n_kv);
 
+/* Storage format of one region of a key cache (dca_attention_window). */
+typedef enum dca_kv_format { DCA_KV_BF16 = 0, DCA_KV_Q8_0 = 1, DCA_KV_Q4_0 = 2 } dca_kv_format;
+
+/* n consecutive cells of every sequence's key cache, in one format:
+ *   DCA_KV_BF16: keys bf16 [B,n,Hkv,D], scales unused (may be NULL);
+ *   DCA_KV_Q8_0: keys int8 codes [B,n,Hkv,D], scales fp16 [B,n,Hkv,D/32] (as dca_attention_q8);
+ *   DCA_KV_Q4_0: keys uint8 codes [B,n,Hkv,D/2], scales fp16 [B,n,Hkv,D/32] (as dca_attention_q4).
+ * The memory may be device memory or pinned host memory (hipHostMalloc or a pinned allocation of
+ * the framework); the caller keeps ownership. */
+typedef struct dca_kv_region {
+  dca_kv_format format;
+  const void* keys;
+  const uint16_t* scales;
+  int32_t n;
+} dca_kv_region;
+
+/* Decode over a key cache split into a window and a tail (the pages' rolling-KV residency: a
+ * window of cells [0, wc) resident on the GPU and the tail [wc, n_kv) spilled to pinned host
+ * memory, read by the DCA decode kernel straight from both regions, each at its own type:
+ * Upstream Sync entries "0111-0113 rolling-KV spill made graceful" (the DCA streaming-tail path)
+ * and "0120-p2-mixed-kv" (a more compressed type for the tail)).
+ * Cells [0, window->n) come from `window`, cells [window->n, window->n + tail->n) from `tail`;
+ * n_kv = window->n + tail->n, and cell j sits at position j as in dca_attention.  The result is
+ * the attention over the whole cache (the split changes nothing but where the bytes are read
+ * from).  A region in host memory is read over the host link by the kernels themselves, with no
+ * staging copy; the library resolves its device address with the HIP runtime and rejects memory
+ * the GPU cannot reach (pageable host memory) with DCA_ERR_INVALID_ARGUMENT.
+ * q, q_pos, o, lse, limits and errors as dca_attention_q8 (split-KV path for every T, bf16 q).
+ * workspace: at least dca_attention_window_workspace_size() bytes of device memory. */
+dca_status dca_attention_window(const dca_config* cfg, int32_t B, int32_t T, const void* q,
+                                const int32_t* q_pos, const dca_kv_region* window,
+                                const dca_kv_region* tail, dca_dtype o_dtype, void* o, float* lse,
+                                void* workspace, size_t ws_bytes, hipStream_t stream);
+size_t dca_attention_window_workspace_size(const dca_config* cfg, int32_t B, int32_t T,
+                                           int32_t n_win, int32_t n_tail);
+
 /* Optional stage timing for dca_attention (measurement hook; no page defines it).  After
  * dca_set_stage_events(ev, n) with n >= DCA_N_STAGE_EVENTS, every dca_attention call made later on
  * this thread records, on its stream: ev[0] before the remap, ev[1] after the remap, ev[2] after

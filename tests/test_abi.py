@@ -135,3 +135,30 @@ def test_q4_entry_point_validation():
                               need, None) == dca.ERR_INVALID_ARGUMENT     # codes missing
     assert L.dca_attention_q4(ctypes.byref(c), 0, 1, None, None, None, None, 4, dca.BF16, None, None,
                               None, 0, None) == dca.OK
+
+
+def test_window_entry_point_validation():
+    """Host-side checks of dca_attention_window that return before any runtime call."""
+    if not os.path.exists(dca.LIB_PATH):
+        pytest.skip("libdca.so not built")
+    L = dca.lib()
+    c = _cfg(chunk=65536)
+    vp = ctypes.c_void_p(16)
+    win = dca._Region(dca.KV_BF16, 16, None, 65536)
+    tail = dca._Region(dca.KV_Q4_0, 16, 16, 196608)
+    need = L.dca_attention_window_workspace_size(ctypes.byref(c), 8, 1, 65536, 196608)
+    # span 4096: 16 window spans + 48 tail spans, 3 regimes of fp32 partials [8*16, 512]
+    assert need >= 3 * 64 * 128 * 512 * 4
+    args = lambda w, t, ws: (ctypes.byref(c), 8, 1, vp, vp, ctypes.byref(w), ctypes.byref(t), dca.BF16,
+                             vp, None, vp, ws, None)
+    assert L.dca_attention_window(*args(win, tail, need - 1)) == dca.ERR_WORKSPACE_TOO_SMALL
+    assert L.dca_attention_window(*args(win, dca._Region(dca.KV_Q4_0, 16, None, 10), need)) \
+        == dca.ERR_INVALID_ARGUMENT                                       # q4_0 region without scales
+    assert L.dca_attention_window(*args(win, dca._Region(7, 16, 16, 10), need)) == dca.ERR_INVALID_ARGUMENT
+    assert L.dca_attention_window(*args(win, dca._Region(dca.KV_BF16, 16, None, -1), need)) \
+        == dca.ERR_INVALID_ARGUMENT
+    assert L.dca_attention_window(ctypes.byref(c), 8, 1, vp, vp, None, ctypes.byref(tail), dca.BF16, vp,
+                                  None, vp, need, None) == dca.ERR_INVALID_ARGUMENT
+    empty = dca._Region(dca.KV_BF16, None, None, 0)
+    assert L.dca_attention_window(ctypes.byref(c), 0, 1, None, None, ctypes.byref(empty),
+                                  ctypes.byref(empty), dca.BF16, None, None, None, 0, None) == dca.OK
