@@ -3,8 +3,9 @@
 One step = one dca_attention call (remap, query rotation x3, key rotation, the three regime passes,
 the N-way merge) on the 32k-token prefill workload (one global layer: 16 query heads, 2 KV heads,
 head_dim 512, chunk 8192, bf16, inputs resident in HBM).  The 256k-KV decode workload (8 sequences,
-chunk 65536) is timed as a second leg, and the same decode over q8_0 and q4_0 key caches as third and
-fourth legs.  Prints one JSON line.
+chunk 65536) is timed as a second leg, the same decode over q8_0 and q4_0 key caches as third and
+fourth legs, and with its cache split into a GPU window and a pinned-host tail as a fifth.  Prints one
+JSON line.
 
 value: query tokens per second of the prefill workload.  roofline: the regime-pass kernel, timed
 live with HIP events recorded by the library between its stages, against the bf16 MFMA peak
@@ -26,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E
+HOST_LINK_PEAK_GBPS = 64.0        # PCIe 5.0 x16, one direction
 
 
 class HipEvents:
@@ -84,11 +86,19 @@ def algorithmic_work(w):
     return flops, kv_bytes
 
 
-def time_leg(torch, dca, w, inp, steps, warmup):
+def time_leg(torch, dca, w, inp, steps, warmup, n_win=None):
+    """Time `steps` calls of the workload's entry point; n_win: bf16 cache split into cells
+    [0, n_win) on the GPU and the rest in pinned host memory (dca_attention_window)."""
     cfg = dca.Config(head_dim=w.D, n_rot=w.n_rot, n_head_q=w.Hq, n_head_kv=w.Hkv, chunk=w.chunk,
                      rope_theta=w.theta, scale=w.scale, freq_factors=to_dev(torch, inp["freq_factors"]))
     q, qp = to_dev(torch, inp["q"]), to_dev(torch, inp["q_pos"])
-    if w.dtype in ("q8_0", "q4_0"):
+    if n_win is not None:
+        kb = torch.from_numpy(inp["k"].view(np.int16)).view(torch.bfloat16)
+        k = (dca.Region(dca.KV_BF16, kb[:, :n_win].contiguous().to("cuda:0")),
+             dca.Region(dca.KV_BF16, kb[:, n_win:].contiguous().pin_memory()))
+        ws_bytes = dca.attention_window_workspace_size(cfg, w.B, w.T, n_win, w.N - n_win)
+        call = dca.attention_window
+    elif w.dtype in ("q8_0", "q4_0"):
         k = (to_dev(torch, inp["k_codes"]), to_dev(torch, inp["k_scales"].view(np.int16)))
         ws_bytes = dca.attention_q8_workspace_size(cfg, w.B, w.T, w.N)
         call = dca.attention_q8 if w.dtype == "q8_0" else dca.attention_q4
@@ -187,10 +197,21 @@ def measured_peaks(torch, dca):
     x.fill_(1)
     t = timed(lambda: dca.probe_hbm_read(x, 8192, sink), 10)
     read = x.numel() / t / 1e9
-    del x, sink
-    return {"mfma_bf16_tflops": mfma, "hbm_read_gbps": read,
+    del x
+    # host link: a 1 GiB copy from pinned host memory, and the same streaming-read kernel reading
+    # pinned host memory in place
+    h = torch.ones((1 << 30,), dtype=torch.uint8).pin_memory()
+    dst = torch.empty((1 << 30,), dtype=torch.uint8, device="cuda:0")
+    t = timed(lambda: dst.copy_(h, non_blocking=True), 5)
+    h2d = h.numel() / t / 1e9
+    t = timed(lambda: dca.probe_hbm_read(h, 8192, sink), 3)
+    host_read = h.numel() / t / 1e9
+    del h, dst, sink
+    return {"mfma_bf16_tflops": mfma, "hbm_read_gbps": read, "host_copy_gbps": h2d,
+            "host_read_gbps": host_read,
             "how": "dca_probe_mfma_bf16 (2048 x 4 waves, 32x32x16 bf16, no memory traffic); "
-                   "dca_probe_hbm_read over 4 GiB"}
+                   "dca_probe_hbm_read over 4 GiB; 1 GiB pinned host -> device copy; "
+                   "dca_probe_hbm_read over 1 GiB of pinned host memory"}
 
 
 def main():
@@ -205,6 +226,10 @@ def main():
     ap.add_argument("--q4-workload", default="decode-b8-kv256k-c65536-q4")
     ap.add_argument("--no-q8", action="store_true")
     ap.add_argument("--no-q4", action="store_true")
+    ap.add_argument("--window-cells", type=int, default=65536,
+                    help="window leg: cells of the 256k decode cache kept on the GPU (the rest in pinned host memory)")
+    ap.add_argument("--window-steps", type=int, default=5)
+    ap.add_argument("--no-window", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -267,6 +292,23 @@ def main():
             "stages_ms": {"remap": std[0], "rope_q": std[1], "tables": std[2],
                           "regime_passes": std[3], "merge": std[4]},
         }
+        if not args.no_window:
+            nw = args.window_cells
+            msw, stw = time_leg(torch, dca, wd, inpd, args.window_steps, 1, n_win=nw)
+            host_bytes = float(wd.B) * (wd.N - nw) * wd.Hkv * wd.D * 2
+            gbw = host_bytes / (stw[3] * 1e-3) / 1e9
+            rec["decode_window"] = {
+                "workload": f"{wd.name}, cells [0, {nw}) on the GPU, [{nw}, {wd.N}) in pinned host memory",
+                "value": wd.B * wd.T / (msw * 1e-3), "unit": "tokens/s", "ms_per_step": msw,
+                "steps": args.window_steps,
+                "roofline": {"bound": "host_link", "achieved": gbw, "peak": HOST_LINK_PEAK_GBPS, "unit": "GB/s",
+                             "frac": gbw / HOST_LINK_PEAK_GBPS, "traffic": None,
+                             "kernel": "attn_decode_kernel over the host tail, then over the window",
+                             "kernel_ms": stw[3], "host_bytes": host_bytes,
+                             "note": "achieved = tail bytes read over the host link / both region passes"},
+                "stages_ms": {"remap": stw[0], "rope_q": stw[1], "tables": stw[2],
+                              "regime_passes": stw[3], "merge": stw[4]},
+            }
         del inpd
     for fmt, name in (("q8", args.q8_workload), ("q4", args.q4_workload)):
         if getattr(args, "no_" + fmt):
@@ -310,6 +352,10 @@ def main():
                 rq = rec[key]["roofline"]
                 rq["measured_peak"] = pk["hbm_read_gbps"]
                 rq["frac_of_measured_peak"] = rq["achieved"] / pk["hbm_read_gbps"]
+        if "decode_window" in rec:
+            rw = rec["decode_window"]["roofline"]
+            rw["measured_peak"] = pk["host_read_gbps"]
+            rw["frac_of_measured_peak"] = rw["achieved"] / pk["host_read_gbps"]
         rec["measured_peaks"] = pk
     if not args.no_cpu_baseline:
         inp = synth.make_inputs(w)

@@ -626,7 +626,10 @@ dca_status dca_probe_hbm_read(const void* src, int64_t bytes, int32_t n_workgrou
     return fail(DCA_ERR_INVALID_ARGUMENT, "bytes must be a non-negative multiple of 16, src 16-byte aligned");
   if (n_workgroups < 1 || n_workgroups > 65536)
     return fail(DCA_ERR_INVALID_ARGUMENT, "n_workgroups %d out of range", n_workgroups);
-  return hip_status(dca::launch_probe_read(src, bytes, n_workgroups, sink, stream), "probe launch");
+  const void* dsrc = src;
+  dca_status st;
+  if (bytes > 0 && (st = device_view(src, &dsrc, "probe source"))) return st;
+  return hip_status(dca::launch_probe_read(dsrc, bytes, n_workgroups, sink, stream), "probe launch");
 }
 
 
