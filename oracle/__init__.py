@@ -39,19 +39,19 @@ def _lib():
         lib.dca_oracle_remap.argtypes = [i64, ctypes.c_int, i64, i32p, i64, i32p, i32p, i32p, ctypes.c_int]
         lib.dca_oracle_rope.restype = None
         lib.dca_oracle_rope.argtypes = [i64, i64, ctypes.c_double, f64p, f64p,
-                                        ctypes.POINTER(ctypes.c_int64), i64, i64, f64p]
+                                        ctypes.POINTER(ctypes.c_int64), i64, i64, f64p, ctypes.c_double]
         lib.dca_oracle_merge.restype = None
         lib.dca_oracle_merge.argtypes = [i64, f64p, f64p, i64, i64, f64p, f64p]
         lib.dca_oracle_attention.restype = ctypes.c_int
         lib.dca_oracle_attention.argtypes = [
             i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_double, ctypes.c_double, f64p, ctypes.c_int,
             ctypes.c_int, i64, i64, ctypes.c_void_p, i32p, ctypes.c_void_p, i64, i64,
-            ctypes.POINTER(ctypes.c_int64), f64p, f64p, f64p, f64p, ctypes.c_int]
+            ctypes.POINTER(ctypes.c_int64), f64p, f64p, f64p, f64p, ctypes.c_int, ctypes.c_double]
         lib.dca_oracle_attention_q8.restype = ctypes.c_int
         lib.dca_oracle_attention_q8.argtypes = [
             i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_double, ctypes.c_double, f64p, ctypes.c_int,
             i64, i64, ctypes.c_void_p, i32p, ctypes.c_void_p, ctypes.c_void_p, i64, i64,
-            ctypes.POINTER(ctypes.c_int64), f64p, f64p, f64p, f64p, ctypes.c_int]
+            ctypes.POINTER(ctypes.c_int64), f64p, f64p, f64p, f64p, ctypes.c_int, ctypes.c_double]
         lib.dca_oracle_half.restype = ctypes.c_double
         lib.dca_oracle_half.argtypes = [ctypes.c_uint16]
         lib.dca_oracle_dequant_q8.restype = None
@@ -101,10 +101,10 @@ def remap(c, qpos, n_kv, n_threads=0, mode=REMAP_BASELINE):
     return pos_q, pos_k, bounds, int(st)
 
 
-def rope(x, pos, n_rot, theta, freq_factors=None):
+def rope(x, pos, n_rot, theta, freq_factors=None, attn_factor=1.0):
     """Partial RoPE of x [rows, H, D] (fp64) at integer positions pos [rows] ("DCA algorithm":
     only the rotary dims move; proportional rope with freq_factors, "Why llamafile is
-    sufficient")."""
+    sufficient"); attn_factor multiplies the rotated dims (YaRN magnitude, 1 = none)."""
     x = np.ascontiguousarray(x, dtype=np.float64)
     rows, H, D = x.shape
     pos = np.ascontiguousarray(np.asarray(pos, dtype=np.int64).reshape(rows))
@@ -112,7 +112,7 @@ def rope(x, pos, n_rot, theta, freq_factors=None):
     ff = None if freq_factors is None else np.ascontiguousarray(freq_factors, dtype=np.float64)
     _lib().dca_oracle_rope(int(n_rot), D, float(theta), None if ff is None else _ptr(ff, ctypes.c_double),
                            _ptr(x, ctypes.c_double), _ptr(pos, ctypes.c_int64), rows, H,
-                           _ptr(y, ctypes.c_double))
+                           _ptr(y, ctypes.c_double), float(attn_factor))
     return y
 
 
@@ -130,7 +130,8 @@ def merge(o_parts, lse_parts):
 
 
 def attention(q, qpos, k, *, chunk, n_rot, theta, scale, freq_factors=None, rows=None,
-              per_regime=True, n_threads=0, round_rotated_bf16=False, remap_mode=REMAP_BASELINE):
+              per_regime=True, n_threads=0, round_rotated_bf16=False, remap_mode=REMAP_BASELINE,
+              attn_factor=1.0):
     """DCA attention of selected query rows in fp64.
 
     q [B, T, Hq, D] and k [B, N, Hkv, D] are float32 arrays or uint16 bf16 bit patterns (same
@@ -165,7 +166,7 @@ def attention(q, qpos, k, *, chunk, n_rot, theta, scale, freq_factors=None, rows
         k.ctypes.data_as(ctypes.c_void_p), N, n, _ptr(sel, ctypes.c_int64),
         _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double),
         None if o_reg is None else _ptr(o_reg, ctypes.c_double),
-        None if lse_reg is None else _ptr(lse_reg, ctypes.c_double), int(n_threads))
+        None if lse_reg is None else _ptr(lse_reg, ctypes.c_double), int(n_threads), float(attn_factor))
     if st != 0:
         raise RuntimeError(f"oracle attention failed with status {st}")
     return dict(o=o, lse=lse, o_reg=o_reg, lse_reg=lse_reg, rows=sel)
@@ -202,7 +203,7 @@ def dequant_q4(codes, scales):
 
 
 def _attention_quant(fn, elems_per_byte, code_dtype, q, qpos, codes, scales, *, chunk, n_rot, theta,
-                     scale, freq_factors, rows, per_regime, n_threads, remap_mode):
+                     scale, freq_factors, rows, per_regime, n_threads, remap_mode, attn_factor):
     q = np.ascontiguousarray(q)
     codes = np.ascontiguousarray(codes, dtype=code_dtype)
     scales = np.ascontiguousarray(scales, dtype=np.uint16)
@@ -230,26 +231,28 @@ def _attention_quant(fn, elems_per_byte, code_dtype, q, qpos, codes, scales, *, 
         codes.ctypes.data_as(ctypes.c_void_p), scales.ctypes.data_as(ctypes.c_void_p), N, n,
         _ptr(sel, ctypes.c_int64), _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double),
         None if o_reg is None else _ptr(o_reg, ctypes.c_double),
-        None if lse_reg is None else _ptr(lse_reg, ctypes.c_double), int(n_threads))
+        None if lse_reg is None else _ptr(lse_reg, ctypes.c_double), int(n_threads), float(attn_factor))
     if st != 0:
         raise RuntimeError(f"oracle attention failed with status {st}")
     return dict(o=o, lse=lse, o_reg=o_reg, lse_reg=lse_reg, rows=sel)
 
 
 def attention_q8(q, qpos, codes, scales, *, chunk, n_rot, theta, scale, freq_factors=None, rows=None,
-                 per_regime=True, n_threads=0, remap_mode=REMAP_BASELINE):
+                 per_regime=True, n_threads=0, remap_mode=REMAP_BASELINE, attn_factor=1.0):
     """DCA attention (as `attention`) over a q8_0 key cache: codes int8 [B, N, Hkv, D], scales
     uint16 fp16 bits [B, N, Hkv, D/32]; the keys (and values, K = V) are d * q.  q is float32 or
     uint16 bf16 bits [B, T, Hq, D]."""
     return _attention_quant(_lib().dca_oracle_attention_q8, 1, np.int8, q, qpos, codes, scales,
                             chunk=chunk, n_rot=n_rot, theta=theta, scale=scale, freq_factors=freq_factors,
-                            rows=rows, per_regime=per_regime, n_threads=n_threads, remap_mode=remap_mode)
+                            rows=rows, per_regime=per_regime, n_threads=n_threads, remap_mode=remap_mode,
+                            attn_factor=attn_factor)
 
 
 def attention_q4(q, qpos, codes, scales, *, chunk, n_rot, theta, scale, freq_factors=None, rows=None,
-                 per_regime=True, n_threads=0, remap_mode=REMAP_BASELINE):
+                 per_regime=True, n_threads=0, remap_mode=REMAP_BASELINE, attn_factor=1.0):
     """DCA attention (as `attention`) over a q4_0 key cache: codes uint8 [B, N, Hkv, D/2] (two
     per byte), scales uint16 fp16 bits [B, N, Hkv, D/32]; the keys (and values) are d * (n - 8)."""
     return _attention_quant(_lib().dca_oracle_attention_q4, 2, np.uint8, q, qpos, codes, scales,
                             chunk=chunk, n_rot=n_rot, theta=theta, scale=scale, freq_factors=freq_factors,
-                            rows=rows, per_regime=per_regime, n_threads=n_threads, remap_mode=remap_mode)
+                            rows=rows, per_regime=per_regime, n_threads=n_threads, remap_mode=remap_mode,
+                            attn_factor=attn_factor)

@@ -47,6 +47,12 @@
  *   y_f = x_f cos a - x_{f+n_rot/2} sin a;  y_{f+n_rot/2} = x_f sin a + x_{f+n_rot/2} cos a.
  *   Dims >= n_rot are copied.  Everything is fp64.
  *
+ * YaRN magnitude factor (attn_factor, default 1): the pages let DCA compose with YaRN's magnitude
+ * scale ("--dca-yarn-factor", fed as the rope's attention factor, [F] "Runtime knobs"; measured
+ * there as no win for retrieval).  Reading: the rotated dims of every query and key are multiplied
+ * by the factor, y_f = m (x_f cos a - ...), so the rotary part of each score scales by m^2; the
+ * pass-through dims and the values (un-rotated keys) are untouched.
+ *
  * Quantized keys (q8_0): the pages run DCA over caches of type q8_0 ([U] entries "DCA all-KV"
  * and "0119-p0-dcaon-scalar-inregister", which read the codes in registers inside the kernel) and
  * give its size as about 0.53x of f16, but print no layout.  Reading: every 32 consecutive dims of
@@ -160,15 +166,16 @@ int64_t dca_oracle_remap(int64_t c, int mode, int64_t n_rows, const int32_t* qpo
   return status;
 }
 
-/* Rotation of one head vector x[0..D) at position p into y (fp64), the RoPE reading above. */
-static void rope_one(int64_t n_rot, int64_t D, double theta, const double* ff, const double* x,
-                     double p, double* y) {
+/* Rotation of one head vector x[0..D) at position p into y (fp64), the RoPE reading above; the
+ * rotated dims are multiplied by mag (the YaRN magnitude factor of the header; 1 = none). */
+static void rope_one(int64_t n_rot, int64_t D, double theta, const double* ff, double mag,
+                     const double* x, double p, double* y) {
   int64_t half = n_rot / 2;
   for (int64_t f = 0; f < half; ++f) {
     double w = pow(theta, -2.0 * (double)f / (double)n_rot);
     if (ff) w /= ff[f];
     double a = p * w;
-    double cs = cos(a), sn = sin(a);
+    double cs = mag * cos(a), sn = mag * sin(a);
     double x0 = x[f], x1 = x[f + half];
     y[f] = x0 * cs - x1 * sn;
     y[f + half] = x0 * sn + x1 * cs;
@@ -178,10 +185,10 @@ static void rope_one(int64_t n_rot, int64_t D, double theta, const double* ff, c
 
 /* Partial RoPE of x [rows][H][D] at pos [rows] into y (fp64). */
 void dca_oracle_rope(int64_t n_rot, int64_t D, double theta, const double* ff, const double* x,
-                     const int64_t* pos, int64_t rows, int64_t H, double* y) {
+                     const int64_t* pos, int64_t rows, int64_t H, double* y, double mag) {
   for (int64_t r = 0; r < rows; ++r)
     for (int64_t h = 0; h < H; ++h)
-      rope_one(n_rot, D, theta, ff, x + (r * H + h) * D, (double)pos[r], y + (r * H + h) * D);
+      rope_one(n_rot, D, theta, ff, mag, x + (r * H + h) * D, (double)pos[r], y + (r * H + h) * D);
 }
 
 /* Element e of an input array that is fp32 (in_bf16 = 0) or bf16 bit patterns (in_bf16 = 1). */
@@ -288,7 +295,8 @@ static int attention_impl(int64_t D, int64_t n_rot, int64_t Hq, int64_t Hkv, int
                           double theta, double scale, const double* ff, int in_bf16, int rot_round,
                           int64_t B, int64_t T, const void* q, const int32_t* qpos, const kv_src* kv,
                           int64_t n_kv, int64_t n_sel, const int64_t* sel, double* o, double* lse,
-                          double* o_reg, double* lse_reg, int n_threads) {
+                          double* o_reg, double* lse_reg, int n_threads, double mag) {
+  if (!(mag > 0.0) || !isfinite(mag)) return -2;
   if (D <= 0 || n_rot <= 0 || n_rot > D || n_rot > 1024 || (n_rot & 1) || Hq <= 0 || Hkv <= 0 ||
       Hq % Hkv || c <= 0 || mode < 0 || mode > 2 || B <= 0 || T <= 0 || n_kv < 0 ||
       (kv->kind >= 2 && (D % 32 || !kv->scales)))
@@ -315,7 +323,7 @@ static int attention_impl(int64_t D, int64_t n_rot, int64_t Hq, int64_t Hkv, int
       for (int64_t g = 0; g < Hkv; ++g) {
         for (int64_t d = 0; d < n_rot; ++d)
           xin[d] = load_k(kv, ((b * n_kv + j) * Hkv + g) * D + d);
-        rope_one(n_rot, n_rot, theta, ff, xin, (double)dca_oracle_key_pos(j, c), xout);
+        rope_one(n_rot, n_rot, theta, ff, mag, xin, (double)dca_oracle_key_pos(j, c), xout);
         if (rot_round == 1)
           for (int64_t d = 0; d < n_rot; ++d) xout[d] = round_bf16(xout[d]);
         memcpy(krot + (j * Hkv + g) * n_rot, xout, sizeof(double) * n_rot);
@@ -342,7 +350,7 @@ static int attention_impl(int64_t D, int64_t n_rot, int64_t Hq, int64_t Hkv, int
           int64_t g = h / G;
           for (int64_t d = 0; d < D; ++d) qv[d] = load_in(q, (flat * Hq + h) * D + d, in_bf16);
           for (int r = 0; r < 3; ++r) {
-            rope_one(n_rot, D, theta, ff, qv, (double)dca_oracle_query_pos(i, c, r, mode), qr + r * D);
+            rope_one(n_rot, D, theta, ff, mag, qv, (double)dca_oracle_query_pos(i, c, r, mode), qr + r * D);
             if (rot_round == 1)
               for (int64_t d = 0; d < n_rot; ++d) qr[r * D + d] = round_bf16(qr[r * D + d]);
           }
@@ -409,10 +417,10 @@ int dca_oracle_attention(int64_t D, int64_t n_rot, int64_t Hq, int64_t Hkv, int6
                          int64_t B,
                          int64_t T, const void* q, const int32_t* qpos, const void* k, int64_t n_kv,
                          int64_t n_sel, const int64_t* sel, double* o, double* lse, double* o_reg,
-                         double* lse_reg, int n_threads) {
+                         double* lse_reg, int n_threads, double attn_factor) {
   kv_src kv = {k, NULL, in_bf16};
   return attention_impl(D, n_rot, Hq, Hkv, c, mode, theta, scale, ff, in_bf16, rot_round, B, T, q,
-                        qpos, &kv, n_kv, n_sel, sel, o, lse, o_reg, lse_reg, n_threads);
+                        qpos, &kv, n_kv, n_sel, sel, o, lse, o_reg, lse_reg, n_threads, attn_factor);
 }
 
 /* The same attention over a q8_0 key cache (codes int8 [B][n_kv][Hkv][D], scales fp16 bits
@@ -421,10 +429,11 @@ int dca_oracle_attention_q8(int64_t D, int64_t n_rot, int64_t Hq, int64_t Hkv, i
                             double theta, double scale, const double* ff, int q_bf16, int64_t B,
                             int64_t T, const void* q, const int32_t* qpos, const int8_t* codes,
                             const uint16_t* scales, int64_t n_kv, int64_t n_sel, const int64_t* sel,
-                            double* o, double* lse, double* o_reg, double* lse_reg, int n_threads) {
+                            double* o, double* lse, double* o_reg, double* lse_reg, int n_threads,
+                            double attn_factor) {
   kv_src kv = {codes, scales, 2};
   return attention_impl(D, n_rot, Hq, Hkv, c, mode, theta, scale, ff, q_bf16, 0, B, T, q, qpos,
-                        &kv, n_kv, n_sel, sel, o, lse, o_reg, lse_reg, n_threads);
+                        &kv, n_kv, n_sel, sel, o, lse, o_reg, lse_reg, n_threads, attn_factor);
 }
 
 /* The same attention over a q4_0 key cache (codes uint8 [B][n_kv][Hkv][D/2], two per byte, scales
@@ -433,8 +442,9 @@ int dca_oracle_attention_q4(int64_t D, int64_t n_rot, int64_t Hq, int64_t Hkv, i
                             double theta, double scale, const double* ff, int q_bf16, int64_t B,
                             int64_t T, const void* q, const int32_t* qpos, const uint8_t* codes,
                             const uint16_t* scales, int64_t n_kv, int64_t n_sel, const int64_t* sel,
-                            double* o, double* lse, double* o_reg, double* lse_reg, int n_threads) {
+                            double* o, double* lse, double* o_reg, double* lse_reg, int n_threads,
+                            double attn_factor) {
   kv_src kv = {codes, scales, 3};
   return attention_impl(D, n_rot, Hq, Hkv, c, mode, theta, scale, ff, q_bf16, 0, B, T, q, qpos,
-                        &kv, n_kv, n_sel, sel, o, lse, o_reg, lse_reg, n_threads);
+                        &kv, n_kv, n_sel, sel, o, lse, o_reg, lse_reg, n_threads, attn_factor);
 }

@@ -257,9 +257,10 @@ def _small_inputs(B, T, N, Hq, Hkv, D, q0, seed, bf16=False):
     return synth.make_inputs(w)
 
 
-def _eager_dca(q, qpos, k, c, n_rot, theta, scale, ff):
+def _eager_dca(q, qpos, k, c, n_rot, theta, scale, ff, mag=1.0):
     """Materialised DCA: three masked dense score blocks and one softmax (the eager form the
-    DCA feature page rules out at scale, "Section-C VERDICT"), with complex-form RoPE."""
+    DCA feature page rules out at scale, "Section-C VERDICT"), with complex-form RoPE; mag
+    multiplies the rotated dims of q and k (YaRN magnitude)."""
     B, T, Hq, D = q.shape
     N, Hkv = k.shape[1], k.shape[2]
     G = Hq // Hkv
@@ -271,10 +272,12 @@ def _eager_dca(q, qpos, k, c, n_rot, theta, scale, ff):
     qpos_r = [np.mod(qpos, c), np.mod(qpos, c) + c, np.full_like(qpos, c - 1)]
     kr = _rope_complex(k.reshape(B * N, Hkv, D), np.tile(np.arange(N) % c, B), n_rot, theta, ff)
     kr = kr.reshape(B, N, Hkv, D)
+    kr[..., :n_rot] *= mag
     S = np.full((B, T, Hq, N), -np.inf)
     for r in range(3):
         qr = _rope_complex(q.reshape(B * T, Hq, D), qpos_r[r].reshape(-1), n_rot, theta, ff)
         qr = qr.reshape(B, T, Hq, D)
+        qr[..., :n_rot] *= mag
         for h in range(Hq):
             s = scale * np.einsum("btd,bnd->btn", qr[:, :, h], kr[:, :, h // G])
             S[:, :, h, :] = np.where(masks[r], s, S[:, :, h, :])
@@ -587,3 +590,38 @@ def test_attention_q4_equals_attention_over_the_dequantized_cache(mode):
     ref = oracle.attention(synth.bf16_to_f32(inp["q"]), inp["q_pos"], kf.astype(np.float32), **kw)
     for key in ("o", "lse", "o_reg", "lse_reg"):
         assert np.array_equal(res[key], ref[key]), key
+
+
+# ----------------------------------------------------------------------------------------------
+# YaRN magnitude factor
+# ----------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mag", [0.5, 1.0, 1.7])
+def test_attention_magnitude_factor_matches_eager_form(mag):
+    """The factor multiplies the rotated dims of q and k: the oracle equals the eager dense form
+    with the complex-form rotations scaled by the factor, and the rope's rotated dims scale by it
+    while the pass-through dims stay bit-exact."""
+    B, T, N, Hq, Hkv, D, q0, c = 1, 21, 30, 4, 2, 32, 9, 6
+    inp = _small_inputs(B, T, N, Hq, Hkv, D, q0, seed=300)
+    q, k, qpos, ff = inp["q"], inp["k"], inp["q_pos"], inp["freq_factors"].astype(np.float64)
+    n_rot, theta, scale = 16, 1.0e6, 0.2
+    res = oracle.attention(q, qpos, k, chunk=c, n_rot=n_rot, theta=theta, scale=scale, freq_factors=ff,
+                           attn_factor=mag)
+    O, lse = _eager_dca(q.astype(np.float64), qpos, k.astype(np.float64), c, n_rot, theta, scale, ff, mag)
+    np.testing.assert_allclose(res["o"], O.reshape(B * T, Hq, D), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(res["lse"], lse.reshape(B * T, Hq), rtol=1e-12)
+    x = q[0].astype(np.float64)
+    y1 = oracle.rope(x, np.arange(T) * 7, n_rot, theta, ff)
+    ym = oracle.rope(x, np.arange(T) * 7, n_rot, theta, ff, attn_factor=mag)
+    np.testing.assert_allclose(ym[..., :n_rot], mag * y1[..., :n_rot], rtol=1e-15, atol=1e-15)
+    assert np.array_equal(ym[..., n_rot:], x[..., n_rot:])
+    if mag != 1.0:   # the factor really changes the result
+        ref = oracle.attention(q, qpos, k, chunk=c, n_rot=n_rot, theta=theta, scale=scale, freq_factors=ff)
+        assert np.abs(ref["lse"] - res["lse"]).max() > 1e-3
+
+
+def test_magnitude_factor_rejected_when_not_positive():
+    inp = _small_inputs(1, 2, 2, 1, 1, 16, 0, seed=301)
+    with pytest.raises(RuntimeError):
+        oracle.attention(inp["q"], inp["q_pos"], inp["k"], chunk=4, n_rot=16, theta=1e6, scale=0.25,
+                         attn_factor=0.0)
