@@ -61,6 +61,8 @@ dca_status check_config(const dca_config* cfg, int dtype) {
   if (!(cfg->rope_theta > 0.0f) || !isfinite(cfg->rope_theta))
     return fail(DCA_ERR_INVALID_ARGUMENT, "rope_theta must be finite and > 0");
   if (!isfinite(cfg->scale)) return fail(DCA_ERR_INVALID_ARGUMENT, "scale must be finite");
+  if (!(cfg->rope_attn_factor > 0.0f) || !isfinite(cfg->rope_attn_factor))
+    return fail(DCA_ERR_INVALID_ARGUMENT, "rope_attn_factor must be finite and > 0");
   if (dtype == DCA_BF16) {
     const int G = cfg->n_head_q / cfg->n_head_kv;
     if (cfg->head_dim != 512 || cfg->n_rot != 128)
@@ -167,6 +169,7 @@ dca::RopeArgs rope_args_for_q(const dca_config* cfg, const void* q, int64_t rows
   ra.planes = 3;
   ra.theta = (double)cfg->rope_theta;
   ra.freq_factors = cfg->freq_factors;
+  ra.mag = (double)cfg->rope_attn_factor;
   return ra;
 }
 
@@ -256,6 +259,7 @@ dca_status dca_rope_partial(const dca_config* cfg, dca_dtype dtype, const void* 
   ra.planes = 1;
   ra.theta = (double)cfg->rope_theta;
   ra.freq_factors = cfg->freq_factors;
+  ra.mag = (double)cfg->rope_attn_factor;
   return hip_status(dca::launch_rope(ra, dtype == DCA_BF16, stream), "rope launch");
 }
 
@@ -406,7 +410,8 @@ dca_status dca_attention(const dca_config* cfg, dca_dtype dtype, int32_t B, int3
     float2* lo = (float2*)(ws + L.tab_lo);
     float2* hi = (float2*)(ws + L.tab_hi);
     if ((st = hip_status(dca::launch_rope_tables(lo, hi, L.n_hi, cfg->n_rot, (double)cfg->rope_theta,
-                                                 cfg->freq_factors, stream), "rope tables launch")))
+                                                 cfg->freq_factors, (double)cfg->rope_attn_factor, stream),
+                       "rope tables launch")))
       return st;
     if ((st = hip_status(mark(3, stream), "stage event"))) return st;
     dca::DecodeArgs da{};
@@ -462,6 +467,7 @@ dca_status dca_attention(const dca_config* cfg, dca_dtype dtype, int32_t B, int3
     rk.out_f16 = 1;
     rk.theta = (double)cfg->rope_theta;
     rk.freq_factors = cfg->freq_factors;
+    rk.mag = (double)cfg->rope_attn_factor;
     if ((st = hip_status(dca::launch_rope(rk, dtype == DCA_BF16, stream), "rope(k) launch"))) return st;
   }
   if ((st = hip_status(mark(3, stream), "stage event"))) return st;
@@ -539,7 +545,8 @@ static dca_status attention_quant(int bits, const dca_config* cfg, int32_t B, in
   float2* lo = (float2*)(ws + L.tab_lo);
   float2* hi = (float2*)(ws + L.tab_hi);
   if ((st = hip_status(dca::launch_rope_tables(lo, hi, L.n_hi, cfg->n_rot, (double)cfg->rope_theta,
-                                               cfg->freq_factors, stream), "rope tables launch")))
+                                               cfg->freq_factors, (double)cfg->rope_attn_factor, stream),
+                       "rope tables launch")))
     return st;
   if ((st = hip_status(mark(3, stream), "stage event"))) return st;
 
@@ -697,7 +704,8 @@ dca_status dca_attention_window(const dca_config* cfg, int32_t B, int32_t T, con
   float2* lo = (float2*)(ws + L.tab_lo);
   float2* hi = (float2*)(ws + L.tab_hi);
   if ((st = hip_status(dca::launch_rope_tables(lo, hi, L.n_hi, cfg->n_rot, (double)cfg->rope_theta,
-                                               cfg->freq_factors, stream), "rope tables launch")))
+                                               cfg->freq_factors, (double)cfg->rope_attn_factor, stream),
+                       "rope tables launch")))
     return st;
   if ((st = hip_status(mark(3, stream), "stage event"))) return st;
 

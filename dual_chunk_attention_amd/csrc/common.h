@@ -106,13 +106,15 @@ struct RopeArgs {
   int32_t planes;
   double theta;
   const float* freq_factors;  // [n_rot/2] or NULL
+  double mag;                 // magnitude factor of the rotated dims (1 = none)
 };
 hipError_t launch_rope(const RopeArgs& a, bool bf16_data, hipStream_t stream);
 
-// cos/sin tables for in-kernel key rotation: lo[64][half] of (cos, sin)(l * w_f) and
-// hi[n_hi][half] of (cos, sin)(64 * h * w_f), both formed from fp64 angles.
+// cos/sin tables for in-kernel key rotation: lo[64][half] of mag * (cos, sin)(l * w_f) and
+// hi[n_hi][half] of (cos, sin)(64 * h * w_f), both formed from fp64 angles (their composition
+// carries the magnitude factor once).
 hipError_t launch_rope_tables(float2* lo, float2* hi, int32_t n_hi, int32_t n_rot, double theta,
-                              const float* freq_factors, hipStream_t stream);
+                              const float* freq_factors, double mag, hipStream_t stream);
 
 // N-way LSE merge.  Part p of row x: o = o_ptr[p] + x*D (pointer mode) or o_base + p*part_stride
 // + x*D (strided mode); lse likewise.

@@ -3,7 +3,8 @@
 // "Why llamafile is sufficient" (per-pair freq_factors fed to the rope), "Section C2b" (keys
 // rotated once, queries three times).  Pair f couples dims f and f + n_rot/2; its angle is
 // p * theta^(-2f/n_rot) / freq_factors[f], formed and reduced in fp64; the rotation itself is
-// fp32 and rounds to nearest-even on a bf16 store.
+// fp32 and rounds to nearest-even on a bf16 store.  The optional magnitude factor (YaRN's
+// attention factor, "Runtime knobs") multiplies the rotated dims: it scales cos and sin in fp64.
 #include "common.h"
 
 namespace dca {
@@ -38,7 +39,7 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeArgs a) {
     }
     double sd, cd;
     sincos((double)p * w_s[f], &sd, &cd);
-    const float cs = (float)cd, sn = (float)sd;
+    const float cs = (float)(a.mag * cd), sn = (float)(a.mag * sd);
     for (int h = 0; h < a.n_heads; ++h) {
       const T* xr = x + row * a.x_row_stride + (int64_t)h * a.x_head_stride;
       TO* yr = y + row * a.y_row_stride + (int64_t)h * a.y_head_stride;
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeArgs a) {
 }
 
 __global__ void rope_tables_kernel(float2* lo, float2* hi, int32_t n_hi, int32_t n_rot,
-                                   double theta, const float* ff) {
+                                   double theta, const float* ff, double mag) {
   const int half = n_rot / 2;
   const int64_t total = (int64_t)(64 + n_hi) * half;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
@@ -75,9 +76,8 @@ __global__ void rope_tables_kernel(float2* lo, float2* hi, int32_t n_hi, int32_t
     const double p = r < 64 ? (double)r : 64.0 * (double)(r - 64);
     double sd, cd;
     sincos(p * w, &sd, &cd);
-    float2 v = make_float2((float)cd, (float)sd);
-    if (r < 64) lo[r * half + f] = v;
-    else hi[(r - 64) * half + f] = v;
+    if (r < 64) lo[r * half + f] = make_float2((float)(mag * cd), (float)(mag * sd));
+    else hi[(r - 64) * half + f] = make_float2((float)cd, (float)sd);
   }
 }
 
@@ -96,12 +96,12 @@ hipError_t launch_rope(const RopeArgs& a, bool bf16_data, hipStream_t stream) {
 }
 
 hipError_t launch_rope_tables(float2* lo, float2* hi, int32_t n_hi, int32_t n_rot, double theta,
-                              const float* freq_factors, hipStream_t stream) {
+                              const float* freq_factors, double mag, hipStream_t stream) {
   int64_t total = (int64_t)(64 + n_hi) * (n_rot / 2);
   int64_t blocks = (total + 255) / 256;
   if (blocks > 2048) blocks = 2048;
   hipLaunchKernelGGL(rope_tables_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, lo, hi,
-                     n_hi, n_rot, theta, freq_factors);
+                     n_hi, n_rot, theta, freq_factors, mag);
   return hipGetLastError();
 }
 

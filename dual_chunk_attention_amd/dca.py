@@ -34,7 +34,7 @@ class _Config(ctypes.Structure):
                 ("n_head_q", ctypes.c_int32), ("n_head_kv", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("remap_mode", ctypes.c_int32),
                 ("rope_theta", ctypes.c_float), ("scale", ctypes.c_float),
-                ("freq_factors", ctypes.c_void_p)]
+                ("freq_factors", ctypes.c_void_p), ("rope_attn_factor", ctypes.c_float)]
 
 
 class _Region(ctypes.Structure):
@@ -103,6 +103,7 @@ class Config:
     scale: Optional[float] = None
     freq_factors: Optional[torch.Tensor] = None
     remap_mode: int = 0
+    rope_attn_factor: float = 1.0
 
     def c(self):
         scale = self.scale if self.scale is not None else (self.head_dim ** -0.5 if self.head_dim > 0 else 1.0)
@@ -111,7 +112,7 @@ class Config:
             assert self.freq_factors.dtype == torch.float32 and self.freq_factors.is_contiguous()
             ff = self.freq_factors.data_ptr()
         return _Config(self.head_dim, self.n_rot, self.n_head_q, self.n_head_kv, self.chunk,
-                       self.remap_mode, self.rope_theta, scale, ff)
+                       self.remap_mode, self.rope_theta, scale, ff, self.rope_attn_factor)
 
 
 def _check(status):

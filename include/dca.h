@@ -103,6 +103,11 @@ typedef struct dca_config {
   float rope_theta;     /* > 0; e.g. 1e6 */
   float scale;          /* score scale, e.g. 1/sqrt(512) */
   const float* freq_factors; /* device fp32 [n_rot/2], each > 0; NULL means all 1.0 */
+  float rope_attn_factor; /* YaRN magnitude factor m on the rotated dims of q and k (the pages'
+                             DCA yarn factor, fed to the rope as its attention factor: DCA feature
+                             page, "Runtime knobs"; measured there as no win, default 1): every
+                             rotated dim is multiplied by m, so the rotary part of a score scales
+                             by m^2; finite and > 0, 1 = none (DCA_ERR_INVALID_ARGUMENT otherwise) */
 } dca_config;
 
 /* Position remap and regime key intervals ("Section C design" table of the DCA feature page;

@@ -52,6 +52,8 @@ def _cfg(**kw):
     (dict(chunk=0), dca.ERR_INVALID_ARGUMENT),
     (dict(remap_mode=3), dca.ERR_INVALID_ARGUMENT),
     (dict(remap_mode=-1), dca.ERR_INVALID_ARGUMENT),
+    (dict(rope_attn_factor=0.0), dca.ERR_INVALID_ARGUMENT),
+    (dict(rope_attn_factor=float("inf")), dca.ERR_INVALID_ARGUMENT),
     (dict(head_dim=256), dca.ERR_UNSUPPORTED),   # bf16 path is head_dim 512 only
     (dict(n_head_q=64, n_head_kv=1), dca.ERR_UNSUPPORTED),
 ])

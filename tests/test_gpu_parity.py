@@ -407,3 +407,36 @@ def test_reference_move_with_extreme_scores(T, N, q0):
     assert res["lse"].max() > 100.0            # scores really are extreme
     assert_o_close(o.cpu().numpy().reshape(-1, 16, 512), res["o"])
     assert_lse_close(lse.cpu().numpy().reshape(-1, 16), res["lse"])
+
+
+# ----------------------------------------------------------------------------------------------
+# YaRN magnitude factor on the rotated dims
+# ----------------------------------------------------------------------------------------------
+
+MAG_CASES = [
+    ("fp32-tiny", "prefill-256-c64-fp32", {}, None, torch.float32),
+    ("bf16-prefill", "prefill-4k-c1024", dict(T=640, N=640), 256, torch.float32),
+    ("bf16-decode", "decode-b8-kv256k-c65536", dict(B=2, N=20000, q0=19999), 4096, torch.float32),
+]
+
+
+@pytest.mark.parametrize("label,name,over,chunk,o_dtype", MAG_CASES, ids=[c[0] for c in MAG_CASES])
+def test_attention_magnitude_factor(label, name, over, chunk, o_dtype):
+    """rope_attn_factor = 1.6 on every path of dca_attention against the oracle with the same
+    factor (the rotary part of each score scales by 2.56)."""
+    inp, w, ffd = _inputs(name, **over)
+    mag = 1.6
+    cfg = cfg_for(w, ffd, chunk=chunk)
+    cfg.rope_attn_factor = mag
+    o, lse = dca.attention(cfg, to_dev(inp["q"]), to_dev(inp["q_pos"]), to_dev(inp["k"]), o_dtype=o_dtype)
+    torch.cuda.synchronize()
+    ff = inp["freq_factors"].astype(np.float64) if w.ff_uniform else None
+    B, T = inp["q"].shape[:2]
+    res = oracle.attention(inp["q"], inp["q_pos"], inp["k"], chunk=cfg.chunk, n_rot=w.n_rot, theta=w.theta,
+                           scale=w.scale, freq_factors=ff, per_regime=False, attn_factor=mag)
+    tol_o, tol_l = (1e-4, 1e-5) if w.dtype == "f32" else (1e-2, 1e-3)
+    assert_o_close(o.float().cpu().numpy().reshape(B * T, w.Hq, w.D), res["o"], atol=tol_o)
+    assert_lse_close(lse.cpu().numpy().reshape(B * T, w.Hq), res["lse"], rtol=tol_l)
+    plain = oracle.attention(inp["q"], inp["q_pos"], inp["k"], chunk=cfg.chunk, n_rot=w.n_rot, theta=w.theta,
+                             scale=w.scale, freq_factors=ff, per_regime=False, rows=[0])
+    assert np.abs(plain["lse"] - res["lse"][:1]).max() > 1e-3      # the factor is not a no-op here

@@ -134,3 +134,21 @@ def test_quant_bitwise_deterministic(fmt):
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quant_magnitude_factor(fmt):
+    """rope_attn_factor = 0.7 through the quantized decode (the factor rides on the cos/sin tables)."""
+    inp = synth.make_inputs(FORMATS[fmt][0], B=2, N=9000, q0=8999)
+    w = inp["w"]
+    B, T, Hq, D = inp["q"].shape
+    cfg = cfg_for(w, to_dev(inp["freq_factors"]), chunk=4096)
+    cfg.rope_attn_factor = 0.7
+    codes, scales = _dev_cache(inp)
+    o, lse = FORMATS[fmt][1](cfg, to_dev(inp["q"]), to_dev(inp["q_pos"]), codes, scales, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    res = FORMATS[fmt][2](inp["q"], inp["q_pos"], inp["k_codes"], inp["k_scales"], chunk=4096, n_rot=w.n_rot,
+                          theta=w.theta, scale=w.scale, freq_factors=inp["freq_factors"].astype(np.float64),
+                          per_regime=False, attn_factor=0.7)
+    assert_o_close(o.cpu().numpy().reshape(B * T, Hq, D), res["o"])
+    assert_lse_close(lse.cpu().numpy().reshape(B * T, Hq), res["lse"])
