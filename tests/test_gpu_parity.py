@@ -440,3 +440,42 @@ def test_attention_magnitude_factor(label, name, over, chunk, o_dtype):
     plain = oracle.attention(inp["q"], inp["q_pos"], inp["k"], chunk=cfg.chunk, n_rot=w.n_rot, theta=w.theta,
                              scale=w.scale, freq_factors=ff, per_regime=False, rows=[0])
     assert np.abs(plain["lse"] - res["lse"][:1]).max() > 1e-3      # the factor is not a no-op here
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(2, 2), (4, 2), (16, 2), (16, 1)])
+def test_gqa_ratios_decode_bf16(Hq, Hkv):
+    """The split-KV decode with G = Hq/Hkv query heads per KV head (the 16 MFMA columns padded)."""
+    w = synth.Workload("gqa-dec", 2, 2, 2998, 3000, 1024, Hq, Hkv, "bf16", 81)
+    inp = synth.make_inputs(w)
+    ffd = to_dev(inp["freq_factors"])
+    o, lse = dca.attention(cfg_for(w, ffd), to_dev(inp["q"]), to_dev(inp["q_pos"]), to_dev(inp["k"]),
+                           o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    res = _oracle_attention(inp, w, per_regime=False)
+    assert_o_close(o.cpu().numpy().reshape(-1, Hq, 512), res["o"])
+    assert_lse_close(lse.cpu().numpy().reshape(-1, Hq), res["lse"])
+
+
+def test_concurrent_streams_with_own_workspaces():
+    """Calls on two streams at once, each with its own workspace, give the results of calls made one
+    after the other (the library keeps no state between calls)."""
+    inp_p, wp, ffp = _inputs("prefill-4k-c1024", T=1024, N=1024)
+    inp_d, wd, ffdd = _inputs("decode-b8-kv256k-c65536", B=2, N=30000, q0=29999)
+    cfg_p, cfg_d = cfg_for(wp, ffp, chunk=256), cfg_for(wd, ffdd, chunk=8192)
+    args_p = (to_dev(inp_p["q"]), to_dev(inp_p["q_pos"]), to_dev(inp_p["k"]))
+    args_d = (to_dev(inp_d["q"]), to_dev(inp_d["q_pos"]), to_dev(inp_d["k"]))
+    o_p1, l_p1 = dca.attention(cfg_p, *args_p)
+    o_d1, l_d1 = dca.attention(cfg_d, *args_d)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            op, lp = dca.attention(cfg_p, *args_p)
+        with torch.cuda.stream(s2):
+            od, ld = dca.attention(cfg_d, *args_d)
+        outs.append((op, lp, od, ld))
+    torch.cuda.synchronize()
+    for op, lp, od, ld in outs:
+        assert torch.equal(op.view(torch.int16), o_p1.view(torch.int16)) and torch.equal(lp, l_p1)
+        assert torch.equal(od.view(torch.int16), o_d1.view(torch.int16)) and torch.equal(ld, l_d1)
