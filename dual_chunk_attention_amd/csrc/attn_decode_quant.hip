@@ -26,7 +26,7 @@
 //    placing it under the fp16 exponent of 1024 (bit pattern 0x6400 | n = 1024 + n) and
 //    subtracting 1032.  One fp16 multiply by d then gives the value (one rounding).
 //  * q4_0 score fragments hold their 8 dims in the order the nibble extraction yields,
-//    (0, 4, 1, 5, 2, 6, 3, 7); the query fragments are stored in the same order.
+//    (0, 2, 4, 6, 1, 3, 5, 7); the query fragments are stored in the same order.
 #include "common.h"
 
 namespace dca {
@@ -81,15 +81,21 @@ __device__ __forceinline__ f16x8 codes8(uint32_t lo, uint32_t hi) {
 #pragma clang diagnostic pop
 
 // eight 4-bit codes of one word (element e at bits 4e..4e+3) -> n - 8 as fp16, in the order
-// (0, 4, 1, 5, 2, 6, 3, 7): the pair (e, e + 4) sits at bits 4e and 4e + 16
+// (0, 2, 4, 6, 1, 3, 5, 7): the low nibbles of the four bytes are the even elements, the high
+// nibbles the odd ones; each byte pair goes under the fp16 exponent of 1024 by one byte permute
 __device__ __forceinline__ f16x8 nibbles8(uint32_t w) {
+  const uint32_t ev = w & 0x0F0F0F0Fu, od = (w >> 4) & 0x0F0F0F0Fu;
   const f16x2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  f16x2 h[4];
+  h[0] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, ev, 0x04010400u)) - off;
+  h[1] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, ev, 0x04030402u)) - off;
+  h[2] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, od, 0x04010400u)) - off;
+  h[3] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, od, 0x04030402u)) - off;
   f16x8 out;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const f16x2 h = __builtin_bit_cast(f16x2, ((w >> (4 * k)) & 0x000F000Fu) | 0x64006400u) - off;
-    out[2 * k] = h[0];
-    out[2 * k + 1] = h[1];
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = h[i][0];
+    out[2 * i + 1] = h[i][1];
   }
   return out;
 }
@@ -115,7 +121,7 @@ __device__ __forceinline__ f16x8 nibble_col8(uint32_t lo, uint32_t hi) {
 }
 
 // position p of a q4_0 score fragment holds element perm4(p) of its 8 dims
-__device__ __forceinline__ constexpr int perm4(int p) { return (p >> 1) + 4 * (p & 1); }
+__device__ __forceinline__ constexpr int perm4(int p) { return 2 * (p & 3) + (p >> 2); }
 
 template <int BITS>
 __device__ __forceinline__ f16x8 order_frag(const f16x8& v) {
