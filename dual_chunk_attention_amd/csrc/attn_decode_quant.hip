@@ -287,8 +287,12 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
       // value operand: transposing reads of rows 32 ks + 8 lg + (lh >> 1), bytes 8 (lh & 1) of a
       // 16-byte chunk; swizzle key = the row's low 4 bits = 8 (lg & 1) + (lh >> 1)
       const int pv_row = 8 * lg + (lh >> 1);
-      const char* vrow = st + pv_row * kRow + 8 * (lh & 1);
       const int pv_key = pv_row & 15;
+      // value chunk j = 8 w + dt (q8_0) or 4 w + bb (q4_0) sits at j ^ pv_key: the wave's bits of j
+      // and the low bits of j occupy disjoint bits, so their XORs are taken apart (one term per
+      // tile, one per block)
+      const char* vrow =
+          st + pv_row * kRow + 8 * (lh & 1) + 16 * (BITS == 8 ? (8 * w) ^ (pv_key & 8) : (4 * w) ^ (pv_key & 12));
 
       // ---- scales: the lane's key row for the scores, and the transposed copy for the values
       f16x8 dsc[2];
@@ -411,13 +415,13 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
             for (int h = 0; h < 2; ++h) {
               const int dt = 2 * bb + h;   // chunk 8 w + dt
               const v2i c = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                  (lds_v2i*)(lds_char*)(vr + 16 * ((8 * w + dt) ^ pv_key)));
+                  (lds_v2i*)(lds_char*)(vr + 16 * (dt ^ (pv_key & 7))));
               o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8((uint32_t)c[0], (uint32_t)c[1]), pd, o[dt], 0, 0, 0);
             }
           } else {
             // chunk 4 w + bb = block 4 w + bb: byte i of the chunk holds dims 2 i and 2 i + 1
             const v2i c = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (lds_v2i*)(lds_char*)(vr + 16 * ((4 * w + bb) ^ pv_key)));
+                (lds_v2i*)(lds_char*)(vr + 16 * (bb ^ (pv_key & 3))));
             o[2 * bb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                 nibble_col8<false>((uint32_t)c[0], (uint32_t)c[1]), pd, o[2 * bb], 0, 0, 0);
             o[2 * bb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
