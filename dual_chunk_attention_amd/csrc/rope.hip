@@ -64,11 +64,11 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeArgs a) {
 }
 
 // Vectorised form for the common case (n_rot/2 a multiple of 8 and at most 128, rows and heads at
-// 16-byte boundaries): a block takes kRopeRows8 rows for every plane and head.  The cos/sin of its
+// 16-byte boundaries): a block takes R rows (8, or 1 when there are few rows) for every plane and
+// head.  The cos/sin of its
 // rows, planes and pairs are formed once into LDS (fp64 angles, the same arithmetic as above), so
 // that each input row is read once for all planes and every thread then moves 8 pairs with
 // 16-byte loads and stores.  Results are bit-identical to rope_kernel.
-constexpr int kRopeRows8 = 8;
 constexpr int kRopeMaxHalf8 = 128;
 constexpr int kRopeMaxPlanes = 3;
 
@@ -102,20 +102,20 @@ __device__ __forceinline__ void store8(float* p, const float* v) {
   *(f32x4*)(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
 }
 
-template <typename T, typename TO>
+template <typename T, typename TO, int R>
 __global__ __launch_bounds__(256) void rope8_kernel(RopeArgs a) {
   __shared__ double w_s[kRopeMaxHalf8];
-  __shared__ float2 tab[kRopeMaxPlanes][kRopeRows8][kRopeMaxHalf8];
+  __shared__ float2 tab[kRopeMaxPlanes][R][kRopeMaxHalf8];
   const int half = a.n_rot / 2;
-  const int64_t row0 = (int64_t)blockIdx.x * kRopeRows8;
+  const int64_t row0 = (int64_t)blockIdx.x * R;
   for (int f = threadIdx.x; f < half; f += blockDim.x) {
     double w = pow(a.theta, -2.0 * (double)f / (double)a.n_rot);
     if (a.freq_factors) w /= (double)a.freq_factors[f];
     w_s[f] = w;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < a.planes * kRopeRows8 * half; e += blockDim.x) {
-    const int z = e / (kRopeRows8 * half), r = (e / half) % kRopeRows8, f = e % half;
+  for (int e = threadIdx.x; e < a.planes * R * half; e += blockDim.x) {
+    const int z = e / (R * half), r = (e / half) % R, f = e % half;
     const int64_t row = row0 + r;
     if (row >= a.rows) continue;
     const int64_t p = a.pos ? (int64_t)a.pos[(int64_t)z * a.pos_plane_stride + row]
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256) void rope8_kernel(RopeArgs a) {
   const T* __restrict__ x = (const T*)a.x;
   const int g8 = half / 8;
   const int per_row = a.n_heads * g8;
-  for (int e = threadIdx.x; e < kRopeRows8 * per_row; e += blockDim.x) {
+  for (int e = threadIdx.x; e < R * per_row; e += blockDim.x) {
     const int r = e / per_row, h = (e % per_row) / g8, f0 = 8 * (e % g8);
     const int64_t row = row0 + r;
     if (row >= a.rows) continue;
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256) void rope8_kernel(RopeArgs a) {
   }
   if (a.copy_tail && sizeof(T) == sizeof(TO)) {
     const int tail = a.head_dim - a.n_rot;
-    const int m = kRopeRows8 * a.n_heads * tail;
+    const int m = R * a.n_heads * tail;
     for (int e = threadIdx.x; e < m; e += blockDim.x) {
       const int64_t row = row0 + e / (a.n_heads * tail);
       const int rem = e % (a.n_heads * tail);
@@ -194,18 +194,26 @@ bool rope8_applies(const RopeArgs& a, bool bf16_data) {
   return in_ok && out_ok;
 }
 
+template <int R>
+void launch_rope8(const RopeArgs& a, bool bf16_data, hipStream_t stream) {
+  const dim3 grid((unsigned)((a.rows + R - 1) / R));
+  if (bf16_data && a.out_f16)
+    hipLaunchKernelGGL((rope8_kernel<bf16, f16, R>), grid, dim3(256), 0, stream, a);
+  else if (bf16_data)
+    hipLaunchKernelGGL((rope8_kernel<bf16, bf16, R>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((rope8_kernel<float, float, R>), grid, dim3(256), 0, stream, a);
+}
+
 }  // namespace
 
 hipError_t launch_rope(const RopeArgs& a, bool bf16_data, hipStream_t stream) {
   if (a.rows <= 0 || a.planes <= 0) return hipSuccess;
   if (rope8_applies(a, bf16_data)) {
-    dim3 grid8((unsigned)((a.rows + kRopeRows8 - 1) / kRopeRows8));
-    if (bf16_data && a.out_f16)
-      hipLaunchKernelGGL((rope8_kernel<bf16, f16>), grid8, dim3(256), 0, stream, a);
-    else if (bf16_data)
-      hipLaunchKernelGGL((rope8_kernel<bf16, bf16>), grid8, dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL((rope8_kernel<float, float>), grid8, dim3(256), 0, stream, a);
+    if (a.rows >= 2048)
+      launch_rope8<8>(a, bf16_data, stream);
+    else   // few rows (decode): one row per block, so that the fp64 angles spread over more blocks
+      launch_rope8<1>(a, bf16_data, stream);
     return hipGetLastError();
   }
   dim3 grid((unsigned)((a.rows + kRopeRows - 1) / kRopeRows), 1, (unsigned)a.planes);
