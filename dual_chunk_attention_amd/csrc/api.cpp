@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <initializer_list>
 #include <string>
 
 #include "../../include/dca.h"
@@ -44,6 +45,16 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 size_t elem_size(dca_dtype t) { return t == DCA_BF16 ? 2 : 4; }
 
 bool valid_dtype(int t) { return t == DCA_F32 || t == DCA_BF16; }
+
+// The kernels move rows with 16-byte loads and stores (direct global->LDS loads included), so the
+// tensors they stream and the workspace start at 16-byte boundaries.  NULL passes (the callers
+// have already rejected a NULL that would be read).
+bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+dca_status check_aligned(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!al16(p)) return fail(DCA_ERR_INVALID_ARGUMENT, "pointer %p is not 16-byte aligned", p);
+  return DCA_OK;
+}
 
 dca_status check_config(const dca_config* cfg, int dtype) {
   if (!cfg) return fail(DCA_ERR_INVALID_ARGUMENT, "config is NULL");
@@ -284,6 +295,7 @@ dca_status dca_attn_regime(const dca_config* cfg, dca_dtype dtype, int32_t regim
   const size_t need = regime_workspace(cfg, dtype, B, T, n_kv);
   if (ws_bytes < need || (need && !workspace))
     return fail(DCA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", ws_bytes, need);
+  if (dtype == DCA_BF16 && (st = check_aligned({q_r, k_rot, k_raw, o_r, workspace}))) return st;
   const size_t es = elem_size(dtype);
   dca::AttnArgs a{};
   for (int r = 0; r < 3; ++r) a.q_rot[r] = q_r;
@@ -379,6 +391,7 @@ dca_status dca_attention(const dca_config* cfg, dca_dtype dtype, int32_t B, int3
     return fail(DCA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", ws_bytes, L.total);
   const bool dec = use_decode(dtype, T);
   if (dec && rows * cfg->n_head_kv > 65535) return fail(DCA_ERR_UNSUPPORTED, "decode batch too large");
+  if (dtype == DCA_BF16 && (st = check_aligned({q, k, o, workspace}))) return st;
   char* ws = (char*)workspace;
   int32_t* pos_q = (int32_t*)(ws + L.pos_q);
   int32_t* bounds = (int32_t*)(ws + L.bounds);
@@ -528,6 +541,7 @@ static dca_status attention_quant(int bits, const dca_config* cfg, int32_t B, in
   const AttnWorkspace L = attention_layout(cfg, DCA_BF16, B, T, n_kv, true);
   if (ws_bytes < L.total || !workspace)
     return fail(DCA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", ws_bytes, L.total);
+  if ((st = check_aligned({q, k_codes, k_scales, o, workspace}))) return st;
   char* ws = (char*)workspace;
   int32_t* pos_q = (int32_t*)(ws + L.pos_q);
   int32_t* bounds = (int32_t*)(ws + L.bounds);
@@ -678,6 +692,8 @@ dca_status dca_attention_window(const dca_config* cfg, int32_t B, int32_t T, con
   const AttnWorkspace L = attention_layout(cfg, DCA_BF16, B, T, n_kv, true, s_all);
   if (ws_bytes < L.total || !workspace)
     return fail(DCA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", ws_bytes, L.total);
+  if ((st = check_aligned({q, o, workspace, window->keys, window->scales, tail->keys, tail->scales})))
+    return st;
   const void* keys[2] = {nullptr, nullptr};
   const void* scales[2] = {nullptr, nullptr};
   for (int i = 0; i < 2; ++i) {

@@ -41,6 +41,10 @@
  *    size is queried first.
  *  - Layouts are row-major, last index fastest: q [B,T,Hq,D], k [B,N,Hkv,D], o [B,T,Hq,D],
  *    lse [B,T,Hq].  Query head h reads KV head h / (Hq/Hkv).
+ *  - The bf16 and quantized paths move rows with 16-byte accesses: their q, k (codes and scales),
+ *    o and workspace pointers must be 16-byte aligned (any allocator's base addresses are), or
+ *    the call returns DCA_ERR_INVALID_ARGUMENT.  The fp32 path takes any naturally aligned
+ *    pointers.
  *  - Work is enqueued on `stream` (NULL = the null stream) with no host synchronisation.
  *  - Arguments are validated on the host before anything is enqueued; a failed check returns a
  *    status, touches nothing, and leaves a message for dca_last_error().  A failing HIP call

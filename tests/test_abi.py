@@ -164,3 +164,37 @@ def test_window_entry_point_validation():
     empty = dca._Region(dca.KV_BF16, None, None, 0)
     assert L.dca_attention_window(ctypes.byref(c), 0, 1, None, None, ctypes.byref(empty),
                                   ctypes.byref(empty), dca.BF16, None, None, None, 0, None) == dca.OK
+
+
+def test_unaligned_pointers_rejected_before_any_launch():
+    """The bf16 and quantized paths stream rows with 16-byte accesses: a pointer off a 16-byte
+    boundary (q, k, codes, scales, o, workspace, region keys) is an invalid argument, caught on the
+    host; the fp32 path takes it."""
+    if not os.path.exists(dca.LIB_PATH):
+        pytest.skip("libdca.so not built")
+    L = dca.lib()
+    c = _cfg()
+    ok, odd = ctypes.c_void_p(4096), ctypes.c_void_p(4096 + 8)
+    need = L.dca_attention_workspace_size(ctypes.byref(c), dca.BF16, 1, 64, 64)
+    for i in range(4):   # q, k, o, workspace in turn
+        p = [ok] * 4
+        p[i] = odd
+        assert L.dca_attention(ctypes.byref(c), dca.BF16, 1, 64, p[0], ok, p[1], 64, dca.BF16, p[2],
+                               None, p[3], need, None) == dca.ERR_INVALID_ARGUMENT
+        assert "16-byte aligned" in L.dca_last_error().decode()
+    need_r = max(L.dca_attn_regime_workspace_size(ctypes.byref(c), dca.BF16, 1, 64, 64), 1)
+    assert L.dca_attn_regime(ctypes.byref(c), dca.BF16, 0, 1, 64, odd, ok, ok, ok, 64, ok, ok, ok,
+                             need_r, None) == dca.ERR_INVALID_ARGUMENT
+    need8 = L.dca_attention_q8_workspace_size(ctypes.byref(c), 1, 1, 64)
+    for i in range(5):   # q, codes, scales, o, workspace
+        p = [ok] * 5
+        p[i] = odd
+        assert L.dca_attention_q8(ctypes.byref(c), 1, 1, p[0], ok, p[1], p[2], 64, dca.BF16, p[3], None,
+                                  p[4], need8, None) == dca.ERR_INVALID_ARGUMENT
+        assert L.dca_attention_q4(ctypes.byref(c), 1, 1, p[0], ok, p[1], p[2], 64, dca.BF16, p[3], None,
+                                  p[4], need8, None) == dca.ERR_INVALID_ARGUMENT
+    needw = L.dca_attention_window_workspace_size(ctypes.byref(c), 1, 1, 32, 32)
+    good = dca._Region(dca.KV_BF16, 4096, None, 32)
+    bad = dca._Region(dca.KV_Q8_0, 4096, 4096 + 8, 32)
+    assert L.dca_attention_window(ctypes.byref(c), 1, 1, ok, ok, ctypes.byref(good), ctypes.byref(bad),
+                                  dca.BF16, ok, None, ok, needw, None) == dca.ERR_INVALID_ARGUMENT
