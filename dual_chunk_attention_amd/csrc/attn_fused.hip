@@ -27,6 +27,8 @@
 //    moves the wave's O, rescaled, into fp32 scratch rows and restarts it at zero; the epilogue
 //    adds the scratch back.
 //  * Workgroups are launched latest query block first (longest causal work first).
+#include <type_traits>
+
 #include "common.h"
 
 namespace dca {
@@ -58,21 +60,27 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
-// One k-step of the score product S^T += K Q^T (32 keys x 32 rows, 16 dims): fp16 for the rotary
-// k-steps 0..7, bf16 for the rest; k-step 0 starts from zero.  Issued as inline asm so that the
-// accumulator stays in VGPRs (the 256 accumulation registers hold O) and every step keeps its place
-// in the issue order.  Hazards the compiler does not see here: two wait states precede each MFMA
-// (a VALU write of an operand just before it), dependent MFMAs on the same accumulator need none,
-// and the caller waits out the last one before the VALU reads the result.
+// Two k-steps s, s+1 of the score product S^T += K Q^T (32 keys x 32 rows, 16 dims each): fp16
+// for the rotary k-steps 0..7, bf16 for the rest; k-step 0 starts from zero.  Issued as inline asm
+// so that the accumulator stays in VGPRs (the 256 accumulation registers hold O) and every step
+// keeps its place in the issue order; two steps per statement halve the hazard waits and the
+// compiler's wait counts in front of them (with one wave per SIMD every instruction costs an issue
+// slot).  Hazards the compiler does not see here: two wait states precede the pair (a VALU write
+// of an operand just before it), dependent MFMAs on the same accumulator need none, and the caller
+// waits out the last one before the VALU reads the result.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void mfma_qk(f32x16& acc, const bf16x8& k, const bf16x8& q, int s) {
+__device__ __forceinline__ void mfma_qk2(f32x16& acc, const bf16x8& k0, const bf16x8& q0, const bf16x8& k1,
+                                         const bf16x8& q1, int s) {
   if (s == 0)
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=v"(acc) : "v"(k), "v"(q));
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, 0\n\tv_mfma_f32_32x32x16_f16 %0, %3, %4, %0"
+                 : "=&v"(acc) : "v"(k0), "v"(q0), "v"(k1), "v"(q1));
   else if (s < 8)
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(k), "v"(q));
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0\n\tv_mfma_f32_32x32x16_f16 %0, %3, %4, %0"
+                 : "+v"(acc) : "v"(k0), "v"(q0), "v"(k1), "v"(q1));
   else
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(k), "v"(q));
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\tv_mfma_f32_32x32x16_bf16 %0, %3, %4, %0"
+                 : "+v"(acc) : "v"(k0), "v"(q0), "v"(k1), "v"(q1));
 }
 #pragma clang diagnostic pop
 
@@ -183,16 +191,42 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
   // ---- tile loads: part j (0..9) of tile k0..k0+31 into the stage at byte offset stg_off, by
   // direct global->LDS loads.  Parts 0..7: raw row 8w+j, lane l the physical chunk l (logical
   // chunk l ^ swz(row)); parts 8..9: four rotated rows 8w+4(j-8)+l/16 each, lane l the physical
-  // chunk l%16.  Rows past the cache re-read its last key (their scores are masked).
+  // chunk l%16.  Rows past the cache re-read its last key (their scores are masked).  A tile
+  // wholly inside the cache (all but the last of a sequence) loads from one scalar base per tile
+  // plus lane offsets computed once before the tile loop: the per-part 64-bit address arithmetic
+  // it replaces cost about 280 scalar and vector instructions per tile and wave, each an issue
+  // slot of the wave's only SIMD slot.
   const bf16* kraw_b = (const bf16*)a.k_raw + ((int64_t)b * a.n_kv * a.Hkv + g) * kD;
   const char* krot_b = (const char*)a.k_rot + ((int64_t)b * a.n_kv * a.Hkv + g) * a.k_rot_hs * 2;
   const int raw_row = a.Hkv * kD * 2, rot_row = a.Hkv * (int)a.k_rot_hs * 2;   // bytes per key
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_char*)smem;
-  auto issue_part = [&](int stg_off, int k0, int j) {
+  // byte offsets of the lane's 16-byte chunk of each load part from the tile's first key (tiles
+  // inside the cache): parts 0..7 raw row 8w + j, parts 8..9 rotated row 8w + 4(j-8) + l/16
+  uint32_t part_off[10];
+#pragma unroll
+  for (int j = 0; j < 10; ++j) {
+    if (j < 8) {
+      const int row = 8 * wu + j;
+      part_off[j] = (uint32_t)(row * raw_row + 16 * (l ^ swz(row)));
+    } else {
+      const int row = 8 * wu + 4 * (j - 8) + (l >> 4);
+      part_off[j] = (uint32_t)(row * rot_row + 16 * ((l & 15) ^ swz(row)));
+    }
+  }
+  auto issue_part = [&](auto inside, int stg_off, int k0, int j) {
     const uint32_t raw_l = smem_lds + stg_off;
     const uint32_t rot_l = raw_l + kRawBytes;
     const int last = a.n_kv - 1 - k0;
     const bool tail = last < kNK - 1;
+    if constexpr (decltype(inside)::value) {
+      if (j < 8)
+        dma16_off(uniform_ptr((const char*)kraw_b + (int64_t)k0 * raw_row), part_off[j],
+                  raw_l + (8 * wu + j) * 1024);
+      else
+        dma16_off(uniform_ptr(krot_b + (int64_t)k0 * rot_row), part_off[j],
+                  rot_l + (8 * wu + 4 * (j - 8)) * 256);
+      return;
+    }
     const int ln = opaque(l);
     if (j < 8) {
       const int row = 8 * wu + j;
@@ -210,8 +244,9 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
 
   // ---- S^T of the tile in the stage at stg_off for the wave's 32 rows: K fragments 4 reads
   // ahead of their MFMA behind scheduling fences; the ten load parts of tile dma_k0 into the
-  // stage at dma_off go out after MFMAs 2, 5, ..., 29 ------------------------------------------
-  auto scores = [&](int stg_off, int dma_off, int dma_k0) {
+  // stage at dma_off go out after MFMA pairs 1, 2, 4, 5, ..., 13, 14 (`inside`: that tile lies
+  // wholly inside the cache, so the loads take the precomputed lane offsets) -----------------
+  auto scores = [&](auto inside, int stg_off, int dma_off, int dma_k0) {
     const char* raw = smem + stg_off + n * 1024;
     const char* rot = smem + stg_off + kRawBytes + n * 256;
     f32x16 acc;
@@ -223,10 +258,14 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
 #pragma unroll
     for (int j = 0; j < kDepthK; ++j) kf[j] = kld(j);
 #pragma unroll
-    for (int s = 0; s < 32; ++s) {
-      mfma_qk(acc, kf[s % kDepthK], q[s], s);
-      if (s + kDepthK < 32) kf[s % kDepthK] = kld(s + kDepthK);
-      if (s % 3 == 2) issue_part(dma_off, dma_k0, s / 3);
+    for (int s = 0; s < 32; s += 2) {
+      mfma_qk2(acc, kf[s % kDepthK], q[s], kf[(s + 1) % kDepthK], q[s + 1], s);
+      if (s + kDepthK < 32) {
+        kf[s % kDepthK] = kld(s + kDepthK);
+        kf[(s + 1) % kDepthK] = kld(s + 1 + kDepthK);
+      }
+      const int p = s / 2;   // load parts after pairs 1, 2, 4, 5, 7, 8, 10, 11, 13, 14
+      if (p % 3 != 0) issue_part(inside, dma_off, dma_k0, p - 1 - p / 3);
       __builtin_amdgcn_sched_barrier(0);
     }
     // the VALU reads the result next: wait out the last MFMA's passes
@@ -332,9 +371,9 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
     // tiles 0 and 1 into stages 0 and 1
     const int k00 = k0_of(0), k01 = k0_of(min(1, n_tiles - 1));
 #pragma unroll
-    for (int j = 0; j < 10; ++j) issue_part(0, k00, j);
+    for (int j = 0; j < 10; ++j) issue_part(std::false_type{}, 0, k00, j);
 #pragma unroll
-    for (int j = 0; j < 10; ++j) issue_part(kStageBytes, k01, j);
+    for (int j = 0; j < 10; ++j) issue_part(std::false_type{}, kStageBytes, k01, j);
     load_qrot(regime_of(0));
   }
   // the Q fragments are complete before the tile loop (its wait counts cannot see the tile loads)
@@ -358,7 +397,9 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
     }
     // scores of tile i, with the loads of tile i+2 (past the end: the last tile again, into a
     // stage no longer read, which keeps ten loads per wave and tile in flight)
-    const f32x16 acc = scores(off_c, off_d, k0_of(min(i + 2, n_tiles - 1)));
+    const int dk0 = k0_of(min(i + 2, n_tiles - 1));
+    const f32x16 acc = a.n_kv - 1 - dk0 >= kNK - 1 ? scores(std::true_type{}, off_c, off_d, dk0)
+                                                   : scores(std::false_type{}, off_c, off_d, dk0);
     float sv[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) sv[e] = acc[e];
