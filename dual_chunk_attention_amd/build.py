@@ -3,11 +3,18 @@
 Every source under csrc/ is compiled to an object in parallel and linked into
 dual_chunk_attention_amd/libdca.so.  Packed fp32 VALU ops are disabled on the device
 (-packed-fp32-ops); hipcc's host pass warns that it does not know the feature, which is harmless.
+The generated code of the sources in HAZARD_CHECKED is checked for the inline-asm MFMA hazards of
+hazards.py; the build fails if one is found.
 """
 import concurrent.futures as cf
 import os
 import subprocess
 import sys
+
+try:
+    from . import hazards
+except ImportError:   # run as a script
+    import hazards
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -25,6 +32,10 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
+# sources whose inline-asm MFMAs rely on hazards.asm_mfma_violations finding nothing
+HAZARD_CHECKED = ["attn_fused.hip"]
+
+
 def _compile(src, verbose):
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
     cmd = ["hipcc", "-c", "-x", "hip", src, "-o", obj] + FLAGS
@@ -40,7 +51,12 @@ def _compile(src, verbose):
 def build(verbose: bool = False, jobs: int = 8) -> str:
     os.makedirs(OBJ, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        checks = [ex.submit(hazards.check_source, os.path.join(CSRC, f), FLAGS) for f in HAZARD_CHECKED]
         results = list(ex.map(lambda s: _compile(s, verbose), sources()))
+        for f, c in zip(HAZARD_CHECKED, checks):
+            n = c.result()   # raises on a violation
+            if verbose:
+                print(f"{f}: {n} inline-asm MFMA blocks free of VALU operand hazards", flush=True)
     for _, out in results:
         if out.strip() and verbose:
             print(out, flush=True)

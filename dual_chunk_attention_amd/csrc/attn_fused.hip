@@ -63,24 +63,42 @@ __device__ __forceinline__ int opaque(int x) {
 // Two k-steps s, s+1 of the score product S^T += K Q^T (32 keys x 32 rows, 16 dims each): fp16
 // for the rotary k-steps 0..7, bf16 for the rest; k-step 0 starts from zero.  Issued as inline asm
 // so that the accumulator stays in VGPRs (the 256 accumulation registers hold O) and every step
-// keeps its place in the issue order; two steps per statement halve the hazard waits and the
-// compiler's wait counts in front of them (with one wave per SIMD every instruction costs an issue
-// slot).  Hazards the compiler does not see here: two wait states precede the pair (a VALU write
-// of an operand just before it), dependent MFMAs on the same accumulator need none, and the caller
-// waits out the last one before the VALU reads the result.
+// keeps its place in the issue order; with one wave per SIMD every instruction costs an issue slot,
+// so the pair carries no wait states of its own.  Hazards the compiler does not see here: an MFMA
+// reading a VGPR that a VALU instruction wrote needs two wait states; the operands come from LDS
+// reads, Q's global loads and earlier MFMAs only, and the build checks the generated code for a
+// VALU write of an operand within two instructions of the pair (dual_chunk_attention_amd/
+// hazards.py).  Dependent MFMAs on the same accumulator need none, and the caller waits out the last
+// one before the VALU reads the result.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void mfma_qk2(f32x16& acc, const bf16x8& k0, const bf16x8& q0, const bf16x8& k1,
                                          const bf16x8& q1, int s) {
   if (s == 0)
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, 0\n\tv_mfma_f32_32x32x16_f16 %0, %3, %4, %0"
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0\n\tv_mfma_f32_32x32x16_f16 %0, %3, %4, %0"
                  : "=&v"(acc) : "v"(k0), "v"(q0), "v"(k1), "v"(q1));
   else if (s < 8)
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0\n\tv_mfma_f32_32x32x16_f16 %0, %3, %4, %0"
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0\n\tv_mfma_f32_32x32x16_f16 %0, %3, %4, %0"
                  : "+v"(acc) : "v"(k0), "v"(q0), "v"(k1), "v"(q1));
   else
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\tv_mfma_f32_32x32x16_bf16 %0, %3, %4, %0"
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\tv_mfma_f32_32x32x16_bf16 %0, %3, %4, %0"
                  : "+v"(acc) : "v"(k0), "v"(q0), "v"(k1), "v"(q1));
+}
+// the same pair with one direct global->LDS load (scalar base sbase + lane offset voff, LDS row
+// address lds_a + lds_b): the M0 write leads, and the two MFMAs are its wait states
+__device__ __forceinline__ void mfma_qk2_load(f32x16& acc, const bf16x8& k0, const bf16x8& q0, const bf16x8& k1,
+                                              const bf16x8& q1, int s, const void* sbase, uint32_t voff,
+                                              uint32_t lds_a, uint32_t lds_b) {
+  if (s < 8)
+    asm volatile("s_add_u32 m0, %5, %6\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0\n\t"
+                 "v_mfma_f32_32x32x16_f16 %0, %3, %4, %0\n\tglobal_load_lds_dwordx4 %7, %8"
+                 : "+v"(acc) : "v"(k0), "v"(q0), "v"(k1), "v"(q1), "s"(lds_a), "s"(lds_b), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+  else
+    asm volatile("s_add_u32 m0, %5, %6\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %0, %3, %4, %0\n\tglobal_load_lds_dwordx4 %7, %8"
+                 : "+v"(acc) : "v"(k0), "v"(q0), "v"(k1), "v"(q1), "s"(lds_a), "s"(lds_b), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -257,15 +275,26 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
     };
 #pragma unroll
     for (int j = 0; j < kDepthK; ++j) kf[j] = kld(j);
+    const char* rawb = uniform_ptr((const char*)kraw_b + (int64_t)dma_k0 * raw_row);
+    const char* rotb = uniform_ptr(krot_b + (int64_t)dma_k0 * rot_row);
+    const uint32_t lds_d = __builtin_amdgcn_readfirstlane(smem_lds + dma_off);
 #pragma unroll
     for (int s = 0; s < 32; s += 2) {
-      mfma_qk2(acc, kf[s % kDepthK], q[s], kf[(s + 1) % kDepthK], q[s + 1], s);
+      const int p = s / 2;   // load parts with pairs 1, 2, 4, 5, 7, 8, 10, 11, 13, 14
+      const int j = p - 1 - p / 3;
+      if (decltype(inside)::value && p % 3 != 0) {
+        const uint32_t lrow = __builtin_amdgcn_readfirstlane(j < 8 ? (8 * wu + j) * 1024
+                                                                    : kRawBytes + (8 * wu + 4 * (j - 8)) * 256);
+        mfma_qk2_load(acc, kf[s % kDepthK], q[s], kf[(s + 1) % kDepthK], q[s + 1], s, j < 8 ? rawb : rotb,
+                      part_off[j], lds_d, lrow);
+      } else {
+        mfma_qk2(acc, kf[s % kDepthK], q[s], kf[(s + 1) % kDepthK], q[s + 1], s);
+      }
       if (s + kDepthK < 32) {
         kf[s % kDepthK] = kld(s + kDepthK);
         kf[(s + 1) % kDepthK] = kld(s + 1 + kDepthK);
       }
-      const int p = s / 2;   // load parts after pairs 1, 2, 4, 5, 7, 8, 10, 11, 13, 14
-      if (p % 3 != 0) issue_part(inside, dma_off, dma_k0, p - 1 - p / 3);
+      if (!decltype(inside)::value && p % 3 != 0) issue_part(inside, dma_off, dma_k0, j);
       __builtin_amdgcn_sched_barrier(0);
     }
     // the VALU reads the result next: wait out the last MFMA's passes
