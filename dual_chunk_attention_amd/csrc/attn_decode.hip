@@ -109,6 +109,17 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(DecodeArgs da) {
       for (int e = 0; e < 8; ++e) lo_q[8 * s + e] = da.rot_lo[qrow * half_rot + 32 * s + 8 * gq + e];
   }
 
+  // byte offset of the lane's 16-byte chunk of each of the wave's tile rows 16w..16w+15 from the
+  // tile's first key, for tiles wholly inside the region (computed once: with one wave per SIMD
+  // every instruction of the per-load address arithmetic is an issue slot of the wave)
+  const int64_t key_bytes = (int64_t)a.Hkv * kD * 2;
+  uint32_t row_off[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int row = 16 * wu + i;
+    row_off[i] = (uint32_t)(row * key_bytes + 16 * (l ^ swz(row)));
+  }
+
   for (int r = 0; r < 3; ++r) {
     if (!(da.regime_mask & (1 << r))) continue;
     const int slot = da.slot0[r] + span;
@@ -141,13 +152,18 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(DecodeArgs da) {
     // its first or last cell (their scores are masked)
     auto issue = [&](int buf, int k0) {
       const uint32_t base = kbuf_lds + buf * kTileBytes;
-      const int64_t key_bytes = (int64_t)a.Hkv * kD * 2;
+      if (k0 >= da.key0 && k0 + kTile <= key_end) {   // the whole tile inside the region
+        const char* src = uniform_ptr((const char*)kraw_b + (int64_t)(k0 - da.key0) * key_bytes);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 16 * wu + i;
-        const int key = min(max(k0 + row, da.key0), key_end - 1);
-        const char* src = uniform_ptr((const char*)kraw_b + (int64_t)(key - da.key0) * key_bytes);
-        dma16(src + 16 * (l ^ swz(row)), base + row * 1024);
+        for (int i = 0; i < 16; ++i) dma16_off(src, row_off[i], base + (16 * wu + i) * 1024);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = 16 * wu + i;
+          const int key = min(max(k0 + row, da.key0), key_end - 1);
+          const char* src = uniform_ptr((const char*)kraw_b + (int64_t)(key - da.key0) * key_bytes);
+          dma16(src + 16 * (l ^ swz(row)), base + row * 1024);
+        }
       }
       if (tab_tile && wu == 0) {   // hi row of the tile (lanes 32..63 fetch the next row, unused)
         const int hr = min((int)((int64_t)k0 % da.chunk >> 6) + (l >> 5), n_hi - 1);
