@@ -231,20 +231,13 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
       part_off[j] = (uint32_t)(row * rot_row + 16 * ((l & 15) ^ swz(row)));
     }
   }
-  auto issue_part = [&](auto inside, int stg_off, int k0, int j) {
+  // the general form (any tile, rows past the cache clamped): the first two tiles and a tile
+  // that reaches past the cache's end; the tiles inside the cache go through mfma_qk2_load
+  auto issue_part = [&](int stg_off, int k0, int j) {
     const uint32_t raw_l = smem_lds + stg_off;
     const uint32_t rot_l = raw_l + kRawBytes;
     const int last = a.n_kv - 1 - k0;
     const bool tail = last < kNK - 1;
-    if constexpr (decltype(inside)::value) {
-      if (j < 8)
-        dma16_off(uniform_ptr((const char*)kraw_b + (int64_t)k0 * raw_row), part_off[j],
-                  raw_l + (8 * wu + j) * 1024);
-      else
-        dma16_off(uniform_ptr(krot_b + (int64_t)k0 * rot_row), part_off[j],
-                  rot_l + (8 * wu + 4 * (j - 8)) * 256);
-      return;
-    }
     const int ln = opaque(l);
     if (j < 8) {
       const int row = 8 * wu + j;
@@ -294,7 +287,7 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
         kf[s % kDepthK] = kld(s + kDepthK);
         kf[(s + 1) % kDepthK] = kld(s + 1 + kDepthK);
       }
-      if (!decltype(inside)::value && p % 3 != 0) issue_part(inside, dma_off, dma_k0, j);
+      if (!decltype(inside)::value && p % 3 != 0) issue_part(dma_off, dma_k0, j);
       __builtin_amdgcn_sched_barrier(0);
     }
     // the VALU reads the result next: wait out the last MFMA's passes
@@ -400,9 +393,9 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
     // tiles 0 and 1 into stages 0 and 1
     const int k00 = k0_of(0), k01 = k0_of(min(1, n_tiles - 1));
 #pragma unroll
-    for (int j = 0; j < 10; ++j) issue_part(std::false_type{}, 0, k00, j);
+    for (int j = 0; j < 10; ++j) issue_part(0, k00, j);
 #pragma unroll
-    for (int j = 0; j < 10; ++j) issue_part(std::false_type{}, kStageBytes, k01, j);
+    for (int j = 0; j < 10; ++j) issue_part(kStageBytes, k01, j);
     load_qrot(regime_of(0));
   }
   // the Q fragments are complete before the tile loop (its wait counts cannot see the tile loads)
