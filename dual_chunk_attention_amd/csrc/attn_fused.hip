@@ -375,11 +375,9 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
   };
 
   // O^T += V^T P^T for the tile in the stage at stg_off, MFMA j = (ks, dt) = (j/16, j%16), V^T
-  // fragments 3 reads ahead behind scheduling fences; `between(j)` runs after MFMA j
-  auto values = [&](int stg_off, const bf16x8* pk, auto&& between) {
-    bf16x8 vf[kDepthV];
-#pragma unroll
-    for (int j = 0; j < kDepthV; ++j) vf[j] = vload(stg_off, j);
+  // fragments 3 reads ahead behind scheduling fences (the first three, vf, read by the caller);
+  // `between(j)` runs after MFMA j
+  auto values = [&](int stg_off, const bf16x8* pk, auto&& between, bf16x8* vf) {
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
       o[j & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j % kDepthV], pk[j >> 4], o[j & 15], 0, 0, 0);
@@ -425,6 +423,11 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
     float sv[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) sv[e] = acc[e];
+    // the first V^T fragments of the tile go out before the softmax, whose VALU work hides their
+    // LDS latency
+    bf16x8 vf[kDepthV];
+#pragma unroll
+    for (int j = 0; j < kDepthV; ++j) vf[j] = vload(off_c, j);
     bf16x8 pk[2];
     float neg_m, psum[4], wsum[2];
     const float alpha = softmax_head(sv, i, pk, neg_m, psum, wsum);
@@ -458,7 +461,7 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
     // after MFMAs 1, 4, 7, 10
     values(off_c, pk, [&](int j) {
       if (j < 12 && j % 3 == 1) exp_pair(sv, 8 + 2 * (j / 3), neg_m, pk, psum, wsum);
-    });
+    }, vf);
     l_part += (psum[0] + psum[1]) + (psum[2] + psum[3]);
     w_part += wsum[0] + wsum[1];
     const int t_off = off_c;
