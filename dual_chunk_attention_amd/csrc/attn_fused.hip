@@ -255,8 +255,9 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
 
   // ---- S^T of the tile in the stage at stg_off for the wave's 32 rows: K fragments 4 reads
   // ahead of their MFMA behind scheduling fences; the ten load parts of tile dma_k0 into the
-  // stage at dma_off go out after MFMA pairs 1, 2, 4, 5, ..., 13, 14 (`inside`: that tile lies
-  // wholly inside the cache, so the loads take the precomputed lane offsets) -----------------
+  // stage at dma_off go out with MFMA pairs 1, 2, 4, 5, ..., 13, 14 (`inside`: that tile lies
+  // wholly inside the cache, so the loads sit in the pairs' asm and take the precomputed lane
+  // offsets; otherwise they follow the pairs in their general, clamped form) ----------------
   auto scores = [&](auto inside, int stg_off, int dma_off, int dma_k0) {
     const char* raw = smem + stg_off + n * 1024;
     const char* rot = smem + stg_off + kRawBytes + n * 256;
