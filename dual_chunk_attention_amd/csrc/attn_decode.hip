@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(DecodeArgs da) {
     // its first or last cell (their scores are masked)
     auto issue = [&](int buf, int k0) {
       const uint32_t base = kbuf_lds + buf * kTileBytes;
-      if (k0 >= da.key0 && k0 + kTile <= key_end) {   // the whole tile inside the region
+      if (k0 >= da.key0 && k0 <= key_end - kTile) {   // the whole tile inside the region
         const char* src = uniform_ptr((const char*)kraw_b + (int64_t)(k0 - da.key0) * key_bytes);
 #pragma unroll
         for (int i = 0; i < 16; ++i) dma16_off(src, row_off[i], base + (16 * wu + i) * 1024);
