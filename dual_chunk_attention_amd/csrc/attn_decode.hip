@@ -155,14 +155,14 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(DecodeArgs da) {
       if (k0 >= da.key0 && k0 <= key_end - kTile) {   // the whole tile inside the region
         const char* src = uniform_ptr((const char*)kraw_b + (int64_t)(k0 - da.key0) * key_bytes);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) dma16_off(src, row_off[i], base + (16 * wu + i) * 1024);
+        for (int i = 0; i < 16; ++i) dma16_off<true>(src, row_off[i], base + (16 * wu + i) * 1024);
       } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int row = 16 * wu + i;
           const int key = min(max(k0 + row, da.key0), key_end - 1);
           const char* src = uniform_ptr((const char*)kraw_b + (int64_t)(key - da.key0) * key_bytes);
-          dma16(src + 16 * (l ^ swz(row)), base + row * 1024);
+          dma16<true>(src + 16 * (l ^ swz(row)), base + row * 1024);
         }
       }
       if (tab_tile && wu == 0) {   // hi row of the tile (lanes 32..63 fetch the next row, unused)

@@ -250,19 +250,19 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
         const uint32_t r0 = __umul24((uint32_t)(16 * wu + hb), key_bytes);
 #pragma unroll
         for (int i = 0; i < 16 / kRpl; ++i)
-          dma16_off(cb, r0 + kRpl * i * key_bytes + (x ^ (16 * kRpl * i)), base + (16 * wu + kRpl * i) * kRow);
+          dma16_off<true>(cb, r0 + kRpl * i * key_bytes + (x ^ (16 * kRpl * i)), base + (16 * wu + kRpl * i) * kRow);
       } else {
 #pragma unroll
         for (int i = 0; i < 16 / kRpl; ++i) {
           const int row = 16 * wu + kRpl * i + hb;
-          dma16_off(cb, __umul24((uint32_t)min(max(row, first), last), key_bytes) + (x ^ (16 * kRpl * i)),
+          dma16_off<true>(cb, __umul24((uint32_t)min(max(row, first), last), key_bytes) + (x ^ (16 * kRpl * i)),
                     base + (16 * wu + kRpl * i) * kRow);
         }
       }
       if (wu < 2) {
         const int row = 32 * wu + (ln >> 1);
         const char* sb = uniform_ptr((const char*)scales_b + (int64_t)(k0 - da.key0) * key_sbytes);
-        dma16_off(sb, __umul24((uint32_t)min(max(row, first), last), key_sbytes) + 16 * (ln & 1),
+        dma16_off<true>(sb, __umul24((uint32_t)min(max(row, first), last), key_sbytes) + 16 * (ln & 1),
                   base + kCodeBytes + wu * 1024);
       }
       if (tab_tile && wu == 2 && ln < 32) {   // hi row of the tile (512 bytes: lanes 0..31)

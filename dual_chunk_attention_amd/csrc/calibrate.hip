@@ -30,16 +30,21 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int32_t iters, float* _
   sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = t;
 }
 
-// 16-byte loads, four in flight per thread per step, grid-stride over n16 = bytes / 16
+// 16-byte nontemporal loads, eight in flight per thread per step, grid-stride over n16 = bytes / 16
+// (of the forms tried on the box: four or eight in flight, with or without the nontemporal hint,
+// 2048 to 32768 workgroups, this one read fastest)
 __global__ __launch_bounds__(256) void probe_read_kernel(const uint4* __restrict__ src, int64_t n16,
                                                          float* __restrict__ sink) {
   uint32_t acc = 0;
   const int64_t stride = (int64_t)gridDim.x * 256;
   int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride], v3 = src[i + 3 * stride];
-    acc ^= v0.x ^ v0.y ^ v0.z ^ v0.w ^ v1.x ^ v1.y ^ v1.z ^ v1.w;
-    acc ^= v2.x ^ v2.y ^ v2.z ^ v2.w ^ v3.x ^ v3.y ^ v3.z ^ v3.w;
+  const u32x4* s4 = (const u32x4*)src;
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    u32x4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = __builtin_nontemporal_load(s4 + i + k * stride);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
   }
   for (; i < n16; i += stride) {
     const uint4 v = src[i];

@@ -42,17 +42,29 @@ typedef __attribute__((address_space(3))) char lds_char;
 // kernels uses M0.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+// NT = true marks the load nontemporal (data read once, such as a decode pass's key cache, which
+// then does not displace reused lines from the caches).
+template <bool NT = false>
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds_row_addr) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_row_addr);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
-               : "memory", "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(lds)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
+                 : "memory", "m0");
 }
 // The same load from a wave-uniform base (scalar registers) plus a 32-bit per-lane byte offset,
 // so that no 64-bit address arithmetic is done per lane.
+template <bool NT = false>
 __device__ __forceinline__ void dma16_off(const void* base, uint32_t off, uint32_t lds_row_addr) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_row_addr);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
-               : "memory", "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(off), "s"(base), "s"(lds)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
+                 : "memory", "m0");
 }
 #pragma clang diagnostic pop
 

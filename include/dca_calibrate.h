@@ -24,7 +24,8 @@ extern "C" {
  * 1 <= n_workgroups <= 65536, 1 <= iters <= 1 << 20; else DCA_ERR_INVALID_ARGUMENT. */
 dca_status dca_probe_mfma_bf16(int32_t n_workgroups, int32_t iters, float* sink, hipStream_t stream);
 
-/* Streaming read of `bytes` at src with 16-byte loads (grid-stride, 4 loads in flight per thread);
+/* Streaming read of `bytes` at src with 16-byte nontemporal loads (grid-stride, 8 loads in flight
+ * per thread);
  * every byte is read once.  src is device memory, or pinned host memory read in place over the host
  * link (pageable host memory: DCA_ERR_INVALID_ARGUMENT).  bytes >= 0 and a multiple of 16, src 16-byte
  * aligned; sink: device fp32 [n_workgroups * 256], written.  1 <= n_workgroups <= 65536. */
