@@ -262,7 +262,9 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
       if (wu < 2) {
         const int row = 32 * wu + (ln >> 1);
         const char* sb = uniform_ptr((const char*)scales_b + (int64_t)(k0 - da.key0) * key_sbytes);
-        dma16_off<true>(sb, __umul24((uint32_t)min(max(row, first), last), key_sbytes) + 16 * (ln & 1),
+        // (not nontemporal: the scale rows of the KV heads share cache lines, which the other
+        // head's workgroup reads as well)
+        dma16_off(sb, __umul24((uint32_t)min(max(row, first), last), key_sbytes) + 16 * (ln & 1),
                   base + kCodeBytes + wu * 1024);
       }
       if (tab_tile && wu == 2 && ln < 32) {   // hi row of the tile (512 bytes: lanes 0..31)
