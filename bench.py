@@ -4,8 +4,9 @@ One step = one dca_attention call (remap, query rotation x3, key rotation, the t
 the N-way merge) on the 32k-token prefill workload (one global layer: 16 query heads, 2 KV heads,
 head_dim 512, chunk 8192, bf16, inputs resident in HBM).  The 256k-KV decode workload (8 sequences,
 chunk 65536) is timed as a second leg, the same decode over q8_0 and q4_0 key caches as third and
-fourth legs, and with its cache split into a GPU window and a pinned-host tail as a fifth.  Prints one
-JSON line.
+fourth legs, and with its cache split into a GPU window and a pinned-host tail as a fifth.  The 4k
+prefill (chunk 1024) and the 1M-key prefill slice (4096 queries at positions [1044480, 1048576)
+against 1048576 keys, chunk 65536) are timed as further prefill legs.  Prints one JSON line.
 
 value: query tokens per second of the prefill workload.  roofline: the regime-pass kernel, timed
 live with HIP events recorded by the library between its stages, against the bf16 MFMA peak
@@ -52,11 +53,11 @@ class HipEvents:
         return float(out.value)
 
 
-def measured_traffic(kernel_file, workload=None):
-    """HBM bytes per launch of a kernel, from the FETCH_SIZE/WRITE_SIZE counter passes recorded in
-    profiles/traffic.json (keyed by the source file, or "file:workload" for a file with several
-    kernels); None when the kernel source changed since the counters were taken."""
-    key = kernel_file if workload is None else f"{kernel_file}:{workload}"
+def measured_traffic(kernel_file, workload):
+    """HBM bytes per launch of a kernel on a workload, from the FETCH_SIZE/WRITE_SIZE counter passes
+    recorded in profiles/traffic.json (keyed "file:workload"); None when there is no record or the
+    kernel source changed since the counters were taken."""
+    key = f"{kernel_file}:{workload}"
     try:
         rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))[key]
         src = open(os.path.join(ROOT, "dual_chunk_attention_amd", "csrc", kernel_file), "rb").read()
@@ -214,6 +215,33 @@ def measured_peaks(torch, dca):
                    "dca_probe_hbm_read over 1 GiB of pinned host memory"}
 
 
+def prefill_leg(torch, dca, synth, name, steps, warmup, cpu_rows):
+    """One prefill workload: tokens/s of whole dca_attention calls, the fused pass's roofline, and
+    (cpu_rows > 0) the oracle timed on a sample of its rows."""
+    w = synth.WORKLOADS[name]
+    inp = synth.make_inputs(w)
+    ms, st = time_leg(torch, dca, w, inp, steps, warmup)
+    flops, _ = algorithmic_work(w)
+    achieved = flops / (st[3] * 1e-3) / 1e12
+    leg = {
+        "workload": w.name, "value": w.B * w.T / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+        "steps": steps,
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "q0": w.q0, "n_kv": w.N, "chunk": w.chunk,
+                   "heads_q": w.Hq, "heads_kv": w.Hkv, "head_dim": w.D, "n_rot": w.n_rot},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": measured_traffic("attn_fused.hip", w.name),
+                     "kernel": "attn_fused_kernel (the three regimes in one pass, one launch)",
+                     "kernel_ms": st[3], "algorithmic_flop": flops},
+        "stages_ms": {"remap": st[0], "rope_q": st[1], "rope_k": st[2], "regime_passes": st[3],
+                      "merge": st[4]},
+    }
+    if cpu_rows > 0:
+        leg["cpu_baseline"] = cpu_baseline(w, inp, cpu_rows)
+    del inp
+    return leg
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -230,7 +258,9 @@ def main():
                     help="window leg: cells of the 256k decode cache kept on the GPU (the rest in pinned host memory)")
     ap.add_argument("--window-steps", type=int, default=5)
     ap.add_argument("--no-window", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--cpu-rows", type=int, default=768)
+    ap.add_argument("--extra-prefill", default="prefill-4k-c1024:512,prefill-4k-at-1m-c65536:4",
+                    help="further prefill legs as workload:cpu_rows, comma-separated ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-measured-peaks", action="store_true")
@@ -268,7 +298,7 @@ def main():
                    "heads_q": w.Hq, "heads_kv": w.Hkv, "head_dim": w.D, "n_rot": w.n_rot},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": measured_traffic("attn_fused.hip") if w.name == "prefill-32k-c8192" else None,
+                     "traffic": measured_traffic("attn_fused.hip", w.name),
                      "kernel": "attn_fused_kernel (the three regimes in one pass, one launch)",
                      "kernel_ms": attn_ms, "algorithmic_flop": flops},
         "stages_ms": {"remap": stages[0], "rope_q": stages[1], "rope_k": stages[2],
@@ -286,7 +316,7 @@ def main():
             "ms_per_step": msd, "steps": args.decode_steps,
             "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": gbps / HBM_PEAK_GBPS,
-                         "traffic": measured_traffic("attn_decode.hip") if wd.name == "decode-b8-kv256k-c65536" else None,
+                         "traffic": measured_traffic("attn_decode.hip", wd.name),
                          "kernel": "attn_decode_kernel (split-KV, 3 regimes)", "kernel_ms": std[3],
                          "algorithmic_bytes": kv_bytes},
             "stages_ms": {"remap": std[0], "rope_q": std[1], "tables": std[2],
@@ -331,6 +361,11 @@ def main():
                           "regime_passes": stq[3], "merge": stq[4]},
         }
         del inpq
+    for spec in [x for x in args.extra_prefill.split(",") if x]:
+        name, _, n_cpu = spec.partition(":")
+        leg = prefill_leg(torch, dca, synth, name, args.steps, args.warmup,
+                          0 if args.no_cpu_baseline else int(n_cpu or 0))
+        rec["prefill_" + name.split("-c")[0].replace("prefill-", "").replace("-", "_")] = leg
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0").fill_(1.0)
         dst = torch.empty_like(src)
@@ -352,6 +387,10 @@ def main():
                 rq = rec[key]["roofline"]
                 rq["measured_peak"] = pk["hbm_read_gbps"]
                 rq["frac_of_measured_peak"] = rq["achieved"] / pk["hbm_read_gbps"]
+        for key in [k for k in rec if k.startswith("prefill_")]:
+            rp = rec[key]["roofline"]
+            rp["measured_peak"] = pk["mfma_bf16_tflops"]
+            rp["frac_of_measured_peak"] = rp["achieved"] / pk["mfma_bf16_tflops"]
         if "decode_window" in rec:
             rw = rec["decode_window"]["roofline"]
             rw["measured_peak"] = pk["host_read_gbps"]

@@ -302,8 +302,8 @@ dca_status dca_attn_regime(const dca_config* cfg, dca_dtype dtype, int32_t regim
   a.q_rot_hs = cfg->head_dim;
   a.q_tail = (const char*)q_r + cfg->n_rot * es;
   a.q_tail_hs = cfg->head_dim;
-  a.k_rot = k_rot;
-  a.k_rot_hs = cfg->head_dim;
+  a.k_rot = k_rot;   // [B,n_kv,Hkv,n_rot]: the rotary dims only
+  a.k_rot_hs = cfg->n_rot;
   a.k_raw = k_raw;
   a.bounds = bounds;
   a.B = B; a.T = T; a.Hq = cfg->n_head_q; a.Hkv = cfg->n_head_kv; a.n_kv = n_kv;

@@ -163,10 +163,11 @@ def rope_partial(cfg: Config, x: torch.Tensor, pos: torch.Tensor, out: Optional[
 
 def attn_regime(cfg: Config, regime: int, q_r: torch.Tensor, bounds: torch.Tensor,
                 k_rot: torch.Tensor, k_raw: torch.Tensor):
-    """dca_attn_regime: q_r [B,T,Hq,D], bounds [3,B,T,2], k_rot/k_raw [B,N,Hkv,D]
-    -> (o_r fp32 [B,T,Hq,D], lse_r fp32 [B,T,Hq])."""
+    """dca_attn_regime: q_r [B,T,Hq,D], bounds [3,B,T,2], k_rot [B,N,Hkv,n_rot] (the rotary dims
+    of the rotated keys), k_raw [B,N,Hkv,D] -> (o_r fp32 [B,T,Hq,D], lse_r fp32 [B,T,Hq])."""
     B, T, Hq, D = q_r.shape
     N = k_raw.shape[1]
+    assert k_rot.shape == (B, N, k_raw.shape[2], cfg.n_rot), (tuple(k_rot.shape), cfg.n_rot)
     for t in (q_r, bounds, k_rot, k_raw):
         assert t.is_contiguous()
     dt = _dtype_code(q_r.dtype)

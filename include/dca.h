@@ -141,7 +141,8 @@ dca_status dca_rope_partial(const dca_config* cfg, dca_dtype dtype, const void* 
  * never 0/0).
  * q_r   : [B,T,Hq,D] queries already rotated at this regime's position (dca_rope_partial).
  * bounds: int32 [3,B,T,2] from dca_remap_positions; only slice `regime` is read.
- * k_rot : [B,n_kv,Hkv,D] keys rotated at pos_k (only the first n_rot dims are read).
+ * k_rot : [B,n_kv,Hkv,n_rot] the rotary dims of the keys, rotated at pos_k (e.g. the first
+ *         n_rot dims of a dca_rope_partial output, made contiguous).
  * k_raw : [B,n_kv,Hkv,D] un-rotated keys, which are also the values.
  * out   : o_r fp32 [B,T,Hq,D], lse_r fp32 [B,T,Hq] (natural log).
  * workspace: device scratch of at least dca_attn_regime_workspace_size() bytes (may be NULL

@@ -1,8 +1,20 @@
 """Helpers shared by the GPU parity tests: moving seeded inputs to the device and the parity bar.
 
-Parity bar (the benchmark spec's tolerance, restated): integer outputs bit-exact; O within 1e-2 absolute;
-LSE within 1e-3 relative (|d lse| <= 1e-3 * max(1, |lse|), a floor so that rows whose LSE is near 0
-are held to 1e-3 absolute); an empty regime must be exactly (0, -inf).
+Parity bar: integer outputs bit-exact; O within 1e-2 absolute; LSE within 1e-3 relative
+(|d lse| <= 1e-3 * max(1, |lse|), a floor so that rows whose LSE is near 0 are held to 1e-3
+absolute); an empty regime must be exactly (0, -inf).
+
+Per-row relative error.  With i.i.d. unit-RMS queries and keys at scale 1/sqrt(512) the scores have
+unit spread, attention is nearly uniform, and |O| per element falls like (e/N)^(1/2): about 0.009
+at 32k keys, 0.003 at 256k, 0.0016 at 1M.  The absolute bound alone then passes an all-zero O.
+So every end-to-end comparison also bounds, for each (row, head), the relative error
+||O_gpu - O_oracle||_2 / ||O_oracle||_2 by O_RTOL = 1e-2.  Derivation: the softmax weights enter the
+value product rounded to bf16 (relative error <= 2^-9 each, independent across keys), and the
+output is rounded to bf16 once more (<= 2^-9 per element); independent roundings of size u give a
+relative error of about u/sqrt(3) ~ 1.1e-3 each in the 2-norm, whatever the number of keys, and
+the fp16 rotated operands move each score by well under 1e-3 (relative weight error of the same
+size).  1e-2 leaves a margin of about 5x over their sum, while a dropped span of keys, a wrong
+rotation or a missing regime moves the ratio by 0.1 to 1.
 """
 import numpy as np
 import torch
@@ -10,6 +22,7 @@ import torch
 from dual_chunk_attention_amd import dca, synth
 
 O_ATOL = 1e-2
+O_RTOL = 1e-2
 LSE_RTOL = 1e-3
 
 
@@ -30,15 +43,34 @@ def cfg_for(w, ff_dev=None, chunk=None, remap_mode=0):
                       freq_factors=ff_dev, remap_mode=remap_mode)
 
 
-def assert_o_close(got, want, atol=O_ATOL, what="O"):
+def row_rel_err(got, want):
+    """||got - want||_2 / ||want||_2 over the last axis (one value per (row, head)); rows whose
+    reference is exactly 0 (empty) give 0 if got is 0 there too, else inf."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    dn = np.sqrt(((got - want) ** 2).sum(axis=-1))
+    wn = np.sqrt((want ** 2).sum(axis=-1))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rel = np.where(wn > 0, dn / np.where(wn > 0, wn, 1.0), np.where(dn > 0, np.inf, 0.0))
+    return rel
+
+
+def assert_o_close(got, want, atol=O_ATOL, rtol=O_RTOL, what="O"):
+    """max|d| <= atol over all elements and ||d||/||O|| <= rtol per (row, head); the message gives
+    both.  Returns (max|d|, max relative row error)."""
     got = np.asarray(got, np.float64)
     want = np.asarray(want, np.float64)
     assert got.shape == want.shape, (got.shape, want.shape)
     assert np.isfinite(got).all(), f"{what}: non-finite values"
     err = np.abs(got - want)
     i = np.unravel_index(np.argmax(err), err.shape)
-    assert err.max() <= atol, f"{what}: max|d| {err.max():.3e} at {i} (got {got[i]}, want {want[i]})"
-    return float(err.max())
+    rel = row_rel_err(got, want)
+    ri = np.unravel_index(np.argmax(rel), rel.shape) if rel.size else ()
+    msg = (f"{what}: max|d| {err.max():.3e} at {i} (got {got[i]}, want {want[i]}); "
+           f"max ||d||/||O|| {rel.max() if rel.size else 0.0:.3e} at row {ri}; max|O| {np.abs(want).max():.3e}")
+    assert err.max() <= atol, msg
+    assert rel.size == 0 or rel.max() <= rtol, msg
+    return float(err.max()), float(rel.max()) if rel.size else 0.0
 
 
 def assert_lse_close(got, want, rtol=LSE_RTOL, what="lse"):

@@ -178,6 +178,7 @@ def test_attn_regime_each_regime(label, name, over, chunk, rows):
     q, k, qp = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["q_pos"])
     pos_q, pos_k, bounds = dca.remap_positions(cfg, qp, N)
     k_rot = dca.rope_partial(cfg, k.reshape(B * N, w.Hkv, w.D), pos_k.repeat(B)).reshape(k.shape)
+    k_rot = k_rot[..., :w.n_rot].contiguous()   # the entry point takes the rotary dims only
     # this entry point receives rotated operands in the data type (bf16 here): the oracle rounds
     # its own fp64 rotations the same way, so the comparison isolates the attention pass
     res = _oracle_attention(inp, w, chunk=c, round_rotated_bf16=w.dtype == "bf16")
