@@ -6,7 +6,10 @@ Each probe first asserts that it bites (the oracle's O is large where the probe 
 then holds the GPU to the usual bar: max|d| <= 1e-2, ||d||/||O|| <= 1e-2 per (row, head), LSE within
 1e-3 relative.  For the distance probe the per-row relative error is also taken over the
 non-rotary dims alone, because the rotary dims of every key (the values, K = V) are one constant
-vector whose norm would otherwise hide an error in which keys win.
+vector whose norm would otherwise hide an error in which keys win.  The distance probe's scores
+spread about ALPHA * scale = 8.5 (a query of rotary norm ALPHA against keys of unit RMS), not 1: its
+LSE is held to 1e-3 of max(8.5, |lse|), since fp16 rotated operands move a score by a fixed fraction
+of that spread whatever value the LSE itself takes.
 """
 import numpy as np
 import pytest
@@ -105,4 +108,5 @@ def test_probe_at_workload_shape(label, name, kind):
     assert_o_close(got_o[sel], want_o)
     if kind == "distance":
         assert_o_close(got_o[sel][..., R:], want_o[..., R:], what="O (non-rotary dims)")
-    assert_lse_close(got_l[sel], want_l)
+    floor = probes.ALPHA * w.scale if kind == "distance" else 1.0
+    assert_lse_close(got_l[sel], want_l, floor=floor)
