@@ -135,9 +135,9 @@ AttnWorkspace attention_layout(const dca_config* cfg, dca_dtype dtype, int32_t B
     w.tab_lo = take((size_t)64 * (R / 2) * 8);
     w.tab_hi = take((size_t)w.n_hi * (R / 2) * 8);
   } else if (dtype == DCA_BF16) {
-    // single fused pass: fp32 rows for O moved out of the registers (regime ends, reference
-    // moves); the final O and lse go straight to the caller's outputs
-    w.o_parts = take(rows * Hq * D * 4);
+    // single fused pass: O stays in registers, the final O and lse go straight to the caller's
+    // outputs; no scratch beyond the positions and rotated operands
+    w.o_parts = take(0);
     w.lse_parts = take(0);
     w.dec_o = w.dec_lse = w.tab_lo = w.tab_hi = off;
   } else {
@@ -491,7 +491,6 @@ dca_status dca_attention(const dca_config* cfg, dca_dtype dtype, int32_t B, int3
   if (dtype == DCA_BF16) {
     // one pass over the three regimes under one online softmax: no partials, no merge
     a.fused = 1;
-    a.o[0] = op;
     a.o_final = o;
     a.o_final_bf16 = o_dtype == DCA_BF16;
     a.lse_final = lse;

@@ -22,10 +22,12 @@
 //    tile's keys are formed between the O^T MFMAs of its first half.
 //  * The key tiles of the three regimes form one sequence (intra, succ, inter); at a regime change
 //    only the rotary Q fragments are reloaded.
-//  * Reference maximum per row: the first tile with a valid key sets it, and it moves only when a
-//    tile exceeds it by more than 64 (log2 units), so exp2 arguments stay <= 64; a move (rare)
-//    moves the wave's O, rescaled, into fp32 scratch rows and restarts it at zero; the epilogue
-//    adds the scratch back.
+//  * Reference maximum per row: the first tile with a valid key sets it, and exp2 arguments stay
+//    <= 64 (log2 units) while no tile exceeds it by more than that.  A tile that does (rare) raises
+//    a flag of the workgroup; after its tile sequence a flagged workgroup runs the sequence twice
+//    more: once with each row's reference following every tile's maximum (its exponents stay <= 0;
+//    its O is discarded), which leaves the exact row maxima, and once more in full against them.
+//    O never leaves the registers before the end, and the pass needs no scratch memory.
 //  * Workgroups are launched latest query block first (longest causal work first).
 #include <type_traits>
 
@@ -107,6 +109,7 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
   constexpr int QB = 128 / G;  // query positions per workgroup
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
   __shared__ int s_lo[3][QB], s_hi[3][QB];
+  __shared__ int s_flag;   // some row's reference maximum must move
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, n = l & 31, half = l >> 5;
@@ -130,6 +133,7 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
     s_lo[r][p] = lo;
     s_hi[r][p] = hi;
   }
+  if (tid == 0) s_flag = 0;
 
   // ---- this lane's query row: rho = 32w + n --------------------------------------------------
   const int rho = 32 * w + n;
@@ -310,12 +314,11 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
 
   // Online-softmax state of the lane's row.  l_part: sum of the exact p (for the LSE); w_part:
   // sum of the bf16-rounded p that the PV product uses (O is normalised by it, so a dominant key's
-  // value comes out exactly).
+  // value comes out exactly).  pass 0: the pass; 1: the reference follows every tile's maximum
+  // (after a flag); 2: the pass again against the exact maxima.
   float m_used = -INFINITY, l_part = 0.0f, w_part = 0.0f;
-  bool flushed = false;   // some of O was moved into the scratch rows (whole wave)
+  int pass = 0;
   f32x16 o[16];
-#pragma unroll
-  for (int dt = 0; dt < 16; ++dt) o[dt] = f32x16{};
 
   // p = exp2(s * scale_log2 - m) for scores e, e+1 into pk: a masked score (-inf) gives 0; a row
   // without any valid key so far has m = -inf and only masked scores, so any finite reference gives
@@ -336,8 +339,8 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
 
   // The scores of tile i (raw, in sv): mask to each row's interval, row maximum, reference of the
   // row (the first tile with a valid key sets it, O of the row being still 0; a tile more than
-  // kTau above it moves it), and the probabilities of keys 0..15 of the tile (pk[0]).  Returns the
-  // factor (1 unless the reference moved) by which the O accumulated so far must be scaled.
+  // kTau above it raises the workgroup's flag), and the probabilities of keys 0..15 of the tile
+  // (pk[0]).
   auto softmax_head = [&](float* sv, int i, bf16x8* pk, float& neg_m, float* psum, float* wsum) {
     const int k0 = k0_of(i);
     if (!(sel(i, full_lo[0], full_lo[1], full_lo[2]) <= k0 &&
@@ -360,19 +363,14 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
       auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       mx = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1])) * scale_log2;
     }
-    const bool first = m_used == -INFINITY;
-    const bool need = !first && mx > m_used + kTau;
-    const float alpha = need ? exp2f(m_used - mx) : 1.0f;
-    if (first || need) m_used = mx;
-    l_part *= alpha;
-    w_part *= alpha;
+    m_used = (pass == 1 || m_used == -INFINITY) ? fmaxf(m_used, mx) : m_used;
+    if (pass == 0 && __ballot(mx > m_used + kTau) != 0 && l == 0) s_flag = 1;
     neg_m = m_used == -INFINITY ? 0.0f : -m_used;
 #pragma unroll
     for (int k = 0; k < 4; ++k) psum[k] = 0.0f;
     wsum[0] = wsum[1] = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; e += 2) exp_pair(sv, e, neg_m, pk, psum, wsum);
-    return alpha;
   };
 
   // O^T += V^T P^T for the tile in the stage at stg_off, MFMA j = (ks, dt) = (j/16, j%16), V^T
@@ -388,90 +386,74 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
     }
   };
 
-  if (n_tiles > 0) {
-    // tiles 0 and 1 into stages 0 and 1
-    const int k00 = k0_of(0), k01 = k0_of(min(1, n_tiles - 1));
+  for (;;) {
 #pragma unroll
-    for (int j = 0; j < 10; ++j) issue_part(0, k00, j);
+    for (int dt = 0; dt < 16; ++dt) o[dt] = f32x16{};
+    l_part = w_part = 0.0f;
+    if (n_tiles > 0) {
+      // tiles 0 and 1 into stages 0 and 1
+      const int k00 = k0_of(0), k01 = k0_of(min(1, n_tiles - 1));
 #pragma unroll
-    for (int j = 0; j < 10; ++j) issue_part(kStageBytes, k01, j);
-    load_qrot(regime_of(0));
-  }
-  // the Q fragments are complete before the tile loop (its wait counts cannot see the tile loads)
-  wait_vm0();
-  int cur_r = n_tiles > 0 ? regime_of(0) : 0;
-  // byte offsets of the stages of tiles i, i+1, i+2 (rotated every tile)
-  int off_c = 0, off_n = kStageBytes, off_d = 2 * kStageBytes;
-
-  for (int i = 0; i < n_tiles; ++i) {
-    // tile i has landed (the ten loads per wave of tile i+1 may still be in flight); the stage of
-    // tile i+2 was last read by the previous tile
-    __builtin_amdgcn_s_waitcnt(0x0F70 | 10);   // vmcnt(10), expcnt and lgkmcnt open
-    __syncthreads();
-    const int r = regime_of(i);
-    if (r != cur_r) {
-      // the compiler's wait counts do not see the tile loads in flight: settle everything so that
-      // the score MFMAs find the new fragments without further waits
-      load_qrot(r);
-      wait_vm0();
-      cur_r = r;
+      for (int j = 0; j < 10; ++j) issue_part(0, k00, j);
+#pragma unroll
+      for (int j = 0; j < 10; ++j) issue_part(kStageBytes, k01, j);
+      load_qrot(regime_of(0));
     }
-    // scores of tile i, with the loads of tile i+2 (past the end: the last tile again, into a
-    // stage no longer read, which keeps ten loads per wave and tile in flight)
-    const int dk0 = k0_of(min(i + 2, n_tiles - 1));
-    const f32x16 acc = a.n_kv - 1 - dk0 >= kNK - 1 ? scores(std::true_type{}, off_c, off_d, dk0)
-                                                   : scores(std::false_type{}, off_c, off_d, dk0);
-    float sv[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) sv[e] = acc[e];
-    // the first V^T fragments of the tile go out before the softmax, whose VALU work hides their
-    // LDS latency
-    bf16x8 vf[kDepthV];
-#pragma unroll
-    for (int j = 0; j < kDepthV; ++j) vf[j] = vload(off_c, j);
-    bf16x8 pk[2];
-    float neg_m, psum[4], wsum[2];
-    const float alpha = softmax_head(sv, i, pk, neg_m, psum, wsum);
-    // the reference of some rows moved: O (tiles up to i-1) of the wave's rows is moved, rescaled,
-    // into their fp32 scratch rows and restarts at zero before tile i adds in (rescaling the 256
-    // accumulation registers in place would need them all in VGPRs at once)
-    if (__ballot(alpha != 1.0f)) {
-      if (row_valid) {
-        float* frow = a.o[0] + rowhead * kD + 4 * half;
-#pragma unroll
-        for (int dt = 0; dt < 16; ++dt) {
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            f32x4 v;
-            v[0] = o[dt][4 * q4 + 0];
-            v[1] = o[dt][4 * q4 + 1];
-            v[2] = o[dt][4 * q4 + 2];
-            v[3] = o[dt][4 * q4 + 3];
-            f32x4* dst = (f32x4*)(frow + 32 * dt + 8 * q4);
-            if (flushed) v += *dst;
-            *dst = v * alpha;
-          }
-        }
+    // the Q fragments are complete before the tile loop (its wait counts cannot see the tile loads)
+    wait_vm0();
+    int cur_r = n_tiles > 0 ? regime_of(0) : 0;
+    // byte offsets of the stages of tiles i, i+1, i+2 (rotated every tile)
+    int off_c = 0, off_n = kStageBytes, off_d = 2 * kStageBytes;
+
+    for (int i = 0; i < n_tiles; ++i) {
+      // tile i has landed (the ten loads per wave of tile i+1 may still be in flight); the stage of
+      // tile i+2 was last read by the previous tile
+      __builtin_amdgcn_s_waitcnt(0x0F70 | 10);   // vmcnt(10), expcnt and lgkmcnt open
+      __syncthreads();
+      const int r = regime_of(i);
+      if (r != cur_r) {
+        // the compiler's wait counts do not see the tile loads in flight: settle everything so
+        // that the score MFMAs find the new fragments without further waits
+        load_qrot(r);
+        wait_vm0();
+        cur_r = r;
       }
+      // scores of tile i, with the loads of tile i+2 (past the end: the last tile again, into a
+      // stage no longer read, which keeps ten loads per wave and tile in flight)
+      const int dk0 = k0_of(min(i + 2, n_tiles - 1));
+      const f32x16 acc = a.n_kv - 1 - dk0 >= kNK - 1 ? scores(std::true_type{}, off_c, off_d, dk0)
+                                                     : scores(std::false_type{}, off_c, off_d, dk0);
+      float sv[16];
 #pragma unroll
-      for (int dt = 0; dt < 16; ++dt) o[dt] = f32x16{};
-      flushed = true;
-      wait_vm0();   // the scratch rows are read back by a later move or the epilogue
+      for (int e = 0; e < 16; ++e) sv[e] = acc[e];
+      // the first V^T fragments of the tile go out before the softmax, whose VALU work hides their
+      // LDS latency
+      bf16x8 vf[kDepthV];
+#pragma unroll
+      for (int j = 0; j < kDepthV; ++j) vf[j] = vload(off_c, j);
+      bf16x8 pk[2];
+      float neg_m, psum[4], wsum[2];
+      softmax_head(sv, i, pk, neg_m, psum, wsum);
+      // O^T of tile i; the probabilities of keys 16..31 (pk[1], first used by MFMA 16) are formed
+      // after MFMAs 1, 4, 7, 10
+      values(off_c, pk, [&](int j) {
+        if (j < 12 && j % 3 == 1) exp_pair(sv, 8 + 2 * (j / 3), neg_m, pk, psum, wsum);
+      }, vf);
+      l_part += (psum[0] + psum[1]) + (psum[2] + psum[3]);
+      w_part += wsum[0] + wsum[1];
+      const int t_off = off_c;
+      off_c = off_n;
+      off_n = off_d;
+      off_d = t_off;
     }
-    // O^T of tile i; the probabilities of keys 16..31 (pk[1], first used by MFMA 16) are formed
-    // after MFMAs 1, 4, 7, 10
-    values(off_c, pk, [&](int j) {
-      if (j < 12 && j % 3 == 1) exp_pair(sv, 8 + 2 * (j / 3), neg_m, pk, psum, wsum);
-    }, vf);
-    l_part += (psum[0] + psum[1]) + (psum[2] + psum[3]);
-    w_part += wsum[0] + wsum[1];
-    const int t_off = off_c;
-    off_c = off_n;
-    off_n = off_d;
-    off_d = t_off;
+    // every wave's flag write and tile loads are complete; the stages may be reloaded
+    wait_vm0();
+    __syncthreads();
+    // a flagged workgroup runs the sequence again: first for the exact row maxima, then in full
+    if (pass == 2 || (pass == 0 && s_flag == 0)) break;
+    ++pass;
   }
 
-  wait_vm0();
   // ---- epilogue: normaliser and natural-log lse from the row totals of both halves ----------
   float l_tot, w_tot;
   {
@@ -483,7 +465,6 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
   const bool nonempty = l_tot > 0.0f && w_tot > 0.0f;
   const float inv = nonempty ? 1.0f / w_tot : 0.0f;
   if (row_valid) {
-    const float* frow = a.o[0] + rowhead * kD + 4 * half;
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt) {
 #pragma unroll
@@ -493,7 +474,6 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
         v[1] = o[dt][4 * q4 + 1];
         v[2] = o[dt][4 * q4 + 2];
         v[3] = o[dt][4 * q4 + 3];
-        if (flushed) v += *(const f32x4*)(frow + 32 * dt + 8 * q4);
         v *= inv;
         const int64_t at = rowhead * kD + 32 * dt + 8 * q4 + 4 * half;
         if (a.o_final_bf16) {

@@ -164,8 +164,7 @@ struct AttnArgs {
   float scale;
   int32_t rot_f16;           // bf16 path: q_rot / k_rot rotary dims are fp16 (else bf16)
   // single pass over the three regimes under one online softmax (bf16 prefill): the final O and
-  // lse go to o_final / lse_final, o[0] is fp32 scratch rows for reference-move flushes only,
-  // o[1], o[2], lse[] are unused
+  // lse go to o_final / lse_final; o[], lse[] are unused
   int32_t fused;
   void* o_final;             // [B*T*Hq][D], bf16 if o_final_bf16 else fp32
   int32_t o_final_bf16;
