@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <initializer_list>
+#include <mutex>
 #include <string>
 
 #include "../../include/dca.h"
@@ -215,6 +216,41 @@ dca_status device_view(const void* p, const void** out, const char* what) {
     return DCA_OK;
   }
   return fail(DCA_ERR_INVALID_ARGUMENT, "%s: unsupported memory type %d", what, (int)at.type);
+}
+
+// ---- scratch of dca_attention_noalloc ------------------------------------------------------
+// A file-scope device array serves as the workspace of the entry point that allocates nothing.
+// Each GPU holds its own copy for the life of the process.  In host code `scratch` is only a
+// stand-in for the symbol: its device address comes from hipGetSymbolAddress, once per device with
+// that device current, and only that address is handed to kernels.
+__device__ __align__(256) char scratch[DCA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];
+
+// Device address of the current device's scratch (looked up on the first call on that device).
+dca_status scratch_address(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(DCA_ERR_UNSUPPORTED, "device %d beyond the %d devices the static scratch serves", dev, kMaxDevices);
+  if (stream) {
+    int sdev = -1;
+    if ((e = hipStreamGetDevice(stream, &sdev)) != hipSuccess) return hip_status(e, "hipStreamGetDevice");
+    if (sdev != dev)
+      return fail(DCA_ERR_INVALID_ARGUMENT, "stream belongs to device %d but device %d is current", sdev, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return hip_status(e, "hipGetSymbolAddress");
+    if (!p) return fail(DCA_ERR_HIP, "hipGetSymbolAddress returned no address for the scratch");
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return DCA_OK;
 }
 
 }  // namespace
@@ -521,6 +557,23 @@ dca_status dca_attention(const dca_config* cfg, dca_dtype dtype, int32_t B, int3
   m.lse_out = lse;
   if ((st = hip_status(dca::launch_merge(m, o_dtype == DCA_BF16, stream), "merge launch"))) return st;
   return hip_status(mark(5, stream), "stage event");
+}
+
+dca_status dca_attention_noalloc(const dca_config* cfg, dca_dtype dtype, int32_t B, int32_t T,
+                                 const void* q, const int32_t* q_pos, const void* k, int32_t n_kv,
+                                 dca_dtype o_dtype, void* o, float* lse, hipStream_t stream) {
+  dca_status st = check_config(cfg, dtype);
+  if (st) return st;
+  if ((st = check_sizes(B, T, n_kv))) return st;
+  if ((int64_t)B * T == 0) return DCA_OK;
+  const size_t need = attention_layout(cfg, dtype, B, T, n_kv).total;
+  if (need > (size_t)DCA_NOALLOC_SCRATCH_BYTES)
+    return fail(DCA_ERR_UNSUPPORTED, "this call needs %zu bytes of scratch; the static scratch holds %zu",
+                need, (size_t)DCA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((st = scratch_address(stream, &ws))) return st;
+  return dca_attention(cfg, dtype, B, T, q, q_pos, k, n_kv, o_dtype, o, lse, ws,
+                       (size_t)DCA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 // dca_attention_q8 / dca_attention_q4: the split-KV decode path over a block-quantized cache

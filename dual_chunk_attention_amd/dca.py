@@ -64,6 +64,8 @@ def lib():
                                     ctypes.c_int, vp, vp, vp]
         L.dca_attention.argtypes = [cfgp, ctypes.c_int, i32, i32, vp, vp, vp, i32, ctypes.c_int, vp,
                                     vp, vp, sz, vp]
+        L.dca_attention_noalloc.argtypes = [cfgp, ctypes.c_int, i32, i32, vp, vp, vp, i32, ctypes.c_int, vp,
+                                            vp, vp]
         L.dca_attention_workspace_size.argtypes = [cfgp, ctypes.c_int, i32, i32, i32]
         L.dca_attention_workspace_size.restype = sz
         L.dca_attention_q8.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, i32, ctypes.c_int, vp, vp, vp,
@@ -84,7 +86,7 @@ def lib():
         L.dca_probe_mfma_bf16.argtypes = [i32, i32, vp, vp]
         L.dca_probe_hbm_read.argtypes = [vp, i64, i32, vp, vp]
         for f in ("dca_remap_positions", "dca_rope_partial", "dca_attn_regime", "dca_lse_merge",
-                  "dca_attention", "dca_attention_q8", "dca_attention_q4", "dca_attention_window",
+                  "dca_attention", "dca_attention_noalloc", "dca_attention_q8", "dca_attention_q4", "dca_attention_window",
                   "dca_probe_mfma_bf16", "dca_probe_hbm_read"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -227,6 +229,24 @@ def attention(cfg: Config, q: torch.Tensor, q_pos: torch.Tensor, k: torch.Tensor
     _check(lib().dca_attention(ctypes.byref(c), dt, B, T, _ptr(q), _ptr(q_pos), _ptr(k), N,
                                _dtype_code(od), _ptr(out), _ptr(lse), _ptr(workspace),
                                workspace.numel(), _stream()))
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # DCA_NOALLOC_SCRATCH_BYTES of include/dca.h
+
+
+def attention_noalloc(cfg: Config, q: torch.Tensor, q_pos: torch.Tensor, k: torch.Tensor,
+                      out: torch.Tensor, lse: torch.Tensor):
+    """dca_attention_noalloc: as attention(), with the library's static scratch as workspace; the
+    caller passes the outputs (o [B,T,Hq,D] of the output dtype, lse fp32 [B,T,Hq])."""
+    B, T, Hq, D = q.shape
+    N = k.shape[1]
+    for t in (q, k, q_pos, out, lse):
+        assert t.is_contiguous()
+    assert q_pos.dtype == torch.int32 and q.dtype == k.dtype and lse.dtype == torch.float32
+    c = cfg.c()
+    _check(lib().dca_attention_noalloc(ctypes.byref(c), _dtype_code(q.dtype), B, T, _ptr(q), _ptr(q_pos),
+                                       _ptr(k), N, _dtype_code(out.dtype), _ptr(out), _ptr(lse), _stream()))
     return out, lse
 
 

@@ -178,6 +178,23 @@ dca_status dca_attention(const dca_config* cfg, dca_dtype dtype, int32_t B, int3
 size_t dca_attention_workspace_size(const dca_config* cfg, dca_dtype dtype, int32_t B, int32_t T,
                                     int32_t n_kv);
 
+/* dca_attention for callers that cannot allocate memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same operation, kernels and results as
+ * dca_attention, with its workspace taken from a static device array of
+ * DCA_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it runs on until the process
+ * ends.  The call allocates nothing (no hipMalloc, no allocating library routine); the caller
+ * still passes q, q_pos, k, o and lse.
+ * A call whose workspace (dca_attention_workspace_size) exceeds DCA_NOALLOC_SCRATCH_BYTES returns
+ * DCA_ERR_UNSUPPORTED before anything is enqueued (e.g. decode over 8 sequences of 256k keys fits,
+ * a 32k-token prefill does not).  `stream` must belong to the current device.
+ * Every call on one GPU shares that GPU's array, which keeps what the last call left there: calls
+ * that overlap on one GPU (on different streams or threads) race and give undefined results;
+ * calls one after the other on a stream are safe.  Other arguments and errors as dca_attention. */
+#define DCA_NOALLOC_SCRATCH_BYTES (64u << 20)
+dca_status dca_attention_noalloc(const dca_config* cfg, dca_dtype dtype, int32_t B, int32_t T,
+                                 const void* q, const int32_t* q_pos, const void* k, int32_t n_kv,
+                                 dca_dtype o_dtype, void* o, float* lse, hipStream_t stream);
+
 /* dca_attention over a key cache stored as q8_0 blocks (the pages run DCA over q8_0 caches and
  * read the codes inside the attention kernel: Upstream Sync entries "DCA all-KV" and
  * "0119-p0-dcaon-scalar-inregister"; they give the size as about 0.53x of f16 but print no
