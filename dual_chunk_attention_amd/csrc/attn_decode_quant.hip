@@ -135,7 +135,9 @@ __device__ __forceinline__ f16x8 order_frag(const f16x8& v) {
   }
 }
 
-template <int BITS>
+// TAB: c is a multiple of 64, so a 64-key tile's positions are p0 + row with p0 a multiple of 64
+// (see the rotation notes at the top)
+template <int BITS, bool TAB>
 __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da) {
   using LY = QLayout<BITS>;
   constexpr int kRow = LY::kRow, kCodeBytes = LY::kCodeBytes, kStageBytes = LY::kStageBytes;
@@ -172,8 +174,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
 
   // query fragments (fp16): B operand lane l holds Q[head hcol][32 s + 8 gq .. +7] (q4_0: in the
   // fragment order); the raw dims come in as bf16 and are converted once into registers, the
-  // rotated dims (s < 4, one set per regime) are read per tile from LDS (head h's 16-byte chunk c
-  // at position c ^ h)
+  // rotated dims (s < 4) are read per tile from LDS (head h's 16-byte chunk c at position c ^ h)
   f16x8 q[16];
   {
     const bf16* qt = (const bf16*)a.q_tail + rowhead * a.q_tail_hs + 8 * gq;
@@ -188,19 +189,43 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
   }
   const int qrow = 16 * w + hcol;   // the lane's key row in the score product
 
-  // Key rotation from the tables (see the bf16 passes): with c a multiple of 64 the lane's lo
-  // entries stay in registers and the tile's hi row travels to LDS with the tile's loads.
   // Fragment position p of the rotary k-steps holds dim 32 s + 8 gq + dim_of(p).
   auto dim_of = [](int p) { return BITS == 8 ? p : perm4(p); };
-  const bool tab_tile = da.chunk % 64 == 0;
+  // TAB: the lane's lo entries (its key row, its 16 pairs) stay in registers
   float2 lo_q[16];
-  if (tab_tile) {
+  if constexpr (TAB) {
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         lo_q[8 * s + e] = da.rot_lo[qrow * half_rot + 32 * s + 8 * gq + dim_of(e)];
   }
+
+  // TAB (G <= 8): thread t turns the query pairs (f, f + 64) and (f + 1, f + 65), f = 2 (t & 31),
+  // of head t >> 5 by minus the tile's hi angles and stores them in qsm (fragment order, chunk
+  // swizzle)
+  auto rotate_query = [&](const f16x2 x0, const f16x2 x1, const float4 hh) {
+    const int t = opaque(tid);
+    const int h = t >> 5, f = 2 * (t & 31);
+    if (h < G) {
+      const float a0 = (float)x0[0], a1 = (float)x0[1];
+      const float b0 = (float)x1[0], b1 = (float)x1[1];
+      const f16x2 y0 = {(_Float16)fmaf(a0, hh.x, b0 * hh.y), (_Float16)fmaf(a1, hh.z, b1 * hh.w)};
+      const f16x2 y1 = {(_Float16)fmaf(b0, hh.x, -a0 * hh.y), (_Float16)fmaf(b1, hh.z, -a1 * hh.w)};
+      char* c0 = qsm + h * 256 + 16 * ((f >> 3) ^ h);
+      char* c1 = qsm + h * 256 + 16 * ((8 + (f >> 3)) ^ h);
+      const int e = f & 7;   // even: elements e, e + 1 of the chunk
+      if constexpr (BITS == 8) {
+        *(f16x2*)(c0 + 2 * e) = y0;
+        *(f16x2*)(c1 + 2 * e) = y1;
+      } else {   // element e sits at position e / 2, element e + 1 at e / 2 + 4
+        ((_Float16*)c0)[e >> 1] = y0[0];
+        ((_Float16*)c0)[(e >> 1) + 4] = y0[1];
+        ((_Float16*)c1)[e >> 1] = y1[0];
+        ((_Float16*)c1)[(e >> 1) + 4] = y1[1];
+      }
+    }
+  };
 
   for (int r = 0; r < 3; ++r) {
     if (!(da.regime_mask & (1 << r))) continue;
@@ -213,13 +238,27 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
       if (tid < G) lse_out[bt * a.Hq + (int64_t)g * G + tid] = -INFINITY;
       continue;
     }
+    const int kt0 = lo / kTile, kt1 = hi / kTile;
+    const _Float16* qrot_r = (const _Float16*)a.q_rot[r];
     {
-      // thread t: head t >> 4, dims 8 (t & 15) .. +7 (fp16 bits, stored in the fragment order)
+      // thread t: head h = t >> 4, dims 8 (t & 15) .. +7 (TAB: only the heads past G, zero)
       const int h = tid >> 4, c = tid & 15;
-      f16x8 v{};
-      if (h < G)
-        v = *(const f16x8*)((const bf16*)a.q_rot[r] + (bt * a.Hq + (int64_t)g * G + h) * a.q_rot_hs + 8 * c);
-      *(f16x8*)(qsm + h * 256 + 16 * (c ^ h)) = order_frag<BITS>(v);
+      if (!TAB || h >= G) {
+        f16x8 v{};
+        if (h < G) v = *(const f16x8*)(qrot_r + (bt * a.Hq + (int64_t)g * G + h) * a.q_rot_hs + 8 * c);
+        *(f16x8*)(qsm + h * 256 + 16 * (c ^ h)) = order_frag<BITS>(v);
+      }
+    }
+    f16x2 qx0 = {}, qx1 = {};   // TAB: the thread's unturned query pairs (see rotate_query)
+    if constexpr (TAB) {
+      const int h = tid >> 5, f = 2 * (tid & 31);
+      if (h < G) {
+        const _Float16* src = qrot_r + (bt * a.Hq + (int64_t)g * G + h) * a.q_rot_hs + f;
+        qx0 = *(const f16x2*)src;
+        qx1 = *(const f16x2*)(src + half_rot);
+      }
+      const int hr = kt0 % (da.chunk / kTile);
+      rotate_query(qx0, qx1, *(const float4*)(da.rot_hi + (int64_t)hr * half_rot + f));
     }
     f32x4 o[8];
 #pragma unroll
@@ -228,13 +267,12 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
     // normaliser, so that weights and normaliser agree)
     float m_used = -INFINITY, l_part = 0.0f, w_part = 0.0f;
 
-    const int kt0 = lo / kTile, kt1 = hi / kTile;
     // tile k0..k0+63 by direct global->LDS loads into stage buf: wave w the code rows
     // 16w..16w+15 (kRpl rows of kRow bytes per load; position p of row r receives global chunk
     // p ^ (r & 15)), waves 0 and 1 the scale rows 0..31 and 32..63 (lane l the half l%2 of row
-    // l/2), lanes 0..31 of wave 2 the hi table row; rows outside the region re-read its first or
-    // last cell (their scores are masked)
-    auto issue = [&](int buf, int k0) {
+    // l/2), lanes 0..31 of wave 2 (TAB) the hi table row of the tile after it; rows outside the
+    // region re-read its first or last cell (their scores are masked)
+    auto issue = [&](int buf, int k0, int hr_next) {
       const uint32_t base = stage_lds + buf * kStageBytes;
       const int ln = opaque(l);
       // tile row r reads region row k0 - key0 + r, clamped to the region: r in [first, last]
@@ -267,12 +305,13 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
         dma16_off(sb, __umul24((uint32_t)min(max(row, first), last), key_sbytes) + 16 * (ln & 1),
                   base + kCodeBytes + wu * 1024);
       }
-      if (tab_tile && wu == 2 && ln < 32) {   // hi row of the tile (512 bytes: lanes 0..31)
-        const int hr = (int)((int64_t)k0 % da.chunk >> 6);
-        dma16_off(uniform_ptr((const char*)(da.rot_hi + (int64_t)hr * half_rot)), 16 * ln, base + kHiRow);
-      }
+      if (TAB && wu == 2 && ln < 32)   // hi row of the next tile (512 bytes: lanes 0..31)
+        dma16_off(uniform_ptr((const char*)(da.rot_hi + (int64_t)hr_next * half_rot)), 16 * ln, base + kHiRow);
     };
-    issue(0, kt0 * kTile);
+    // TAB: tile kt's hi row is kt mod (c / 64); hr_ld follows the tile after the one being issued
+    const int n_hi = TAB ? da.chunk / kTile : 1;
+    int hr_ld = (kt0 + 1) % n_hi;
+    issue(0, kt0 * kTile, hr_ld);
 
     for (int kt = kt0; kt <= kt1; ++kt) {
       const int cur = (kt - kt0) & 1;
@@ -280,28 +319,43 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
       // tile kt has landed (every wave's loads) and every wave is done with tile kt - 1
       wait_vm0();
       __syncthreads();
-      if (kt < kt1) issue(cur ^ 1, k0 + kTile);
+      if (kt < kt1) {
+        hr_ld = hr_ld + 1 == n_hi ? 0 : hr_ld + 1;
+        issue(cur ^ 1, k0 + kTile, hr_ld);
+      }
       const char* st = stage + cur * kStageBytes;
       // lane-dependent offsets, recomputed per tile
       const int ln = opaque(l);
       const int lh = ln & 15, lg = ln >> 4;
       const int lrow = 16 * w + lh;
-      // value operand: transposing reads of rows 32 ks + 8 lg + (lh >> 1), bytes 8 (lh & 1) of a
-      // 16-byte chunk; swizzle key = the row's low 4 bits = 8 (lg & 1) + (lh >> 1)
-      const int pv_row = 8 * lg + (lh >> 1);
-      const int pv_key = pv_row & 15;
-      // value chunk j = 8 w + dt (q8_0) or 4 w + bb (q4_0) sits at j ^ pv_key: the wave's bits of j
-      // and the low bits of j occupy disjoint bits, so their XORs are taken apart (one term per
-      // tile, one per block)
-      const char* vrow =
-          st + pv_row * kRow + 8 * (lh & 1) + 16 * (BITS == 8 ? (8 * w) ^ (pv_key & 8) : (4 * w) ^ (pv_key & 12));
 
-      // ---- scales: the lane's key row for the scores, and the transposed copy for the values
+      // ---- score operands, all read before any is used: the lane's key row of codes (dims
+      // 32 s + 8 lg .. +7 for k-step s) and scales, the rotated query, the transposed scales' source
+      const char* krow = st + lrow * kRow;
       f16x8 dsc[2];
       dsc[0] = *(const f16x8*)(st + kCodeBytes + lrow * 32);
       dsc[1] = *(const f16x8*)(st + kCodeBytes + lrow * 32 + 16);
+      const uint2 d4 = *(const uint2*)(st + kCodeBytes + lrow * 32 + 8 * lg);   // blocks 4lg..+3
+      uint2 cw[16];   // q8_0: 8 codes; q4_0: 8 codes in .x
+      if constexpr (BITS == 8) {
+        // chunk (2 s + (lg >> 1)) ^ lh, bytes 8 (lg & 1): with s = 8 t + u that is byte
+        // 16 ((lg >> 1) ^ (lh & 1)) + 32 (u ^ (lh >> 1)) + 256 t, so 8 addresses serve 16 reads
+        const char* kb = krow + 8 * (lg & 1) + 16 * ((lg >> 1) ^ (lh & 1));
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const char* p = kb + 32 * (u ^ (lh >> 1));
+          cw[u] = *(const uint2*)p;
+          cw[u + 8] = *(const uint2*)(p + 256);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 16; ++s) cw[s].x = *(const uint32_t*)(krow + 4 * lg + 16 * (s ^ lh));   // chunk s, bytes 4 lg
+      }
+      f16x8 qs[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) qs[s] = *(const f16x8*)(qsm + lh * 256 + 16 * ((4 * s + lg) ^ lh));
+      __builtin_amdgcn_sched_barrier(0);
       {
-        const uint2 d4 = *(const uint2*)(st + kCodeBytes + lrow * 32 + 8 * lg);   // blocks 4lg..+3
         uint16_t* t = (uint16_t*)sT + 4 * lg * kTile + lrow;
         t[0 * kTile] = (uint16_t)d4.x;
         t[1 * kTile] = (uint16_t)(d4.x >> 16);
@@ -313,75 +367,73 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
       auto kfrag = [&](int s) {
         const _Float16 d = dsc[s >> 3][s & 7];
         const f16x8 dd = {d, d, d, d, d, d, d, d};
-        if constexpr (BITS == 8) {
-          // dims 32 s + 8 lg .. +7: chunk 2 s + (lg >> 1), bytes 8 (lg & 1)
-          const uint2 c8 = *(const uint2*)(st + lrow * kRow + 8 * (lg & 1) + 16 * ((2 * s + (lg >> 1)) ^ lh));
-          return codes8(c8.x, c8.y) * dd;
-        } else {
-          // dims 32 s + 8 lg .. +7: chunk s, bytes 4 lg
-          const uint32_t c4 = *(const uint32_t*)(st + lrow * kRow + 4 * lg + 16 * (s ^ lh));
-          return nibbles8(c4) * dd;
-        }
+        if constexpr (BITS == 8)
+          return codes8(cw[s].x, cw[s].y) * dd;
+        else
+          return nibbles8(cw[s].x) * dd;
       };
       f32x4 sacc = f32x4{};
       {
         f16x8 kr[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) kr[s] = kfrag(s);
-        // rotate the rotary pairs (f, f + 64) of the lane's key by (cos, sin) of pos * w_f,
-        // composed from the lo and hi tables by the angle-addition formulas
-        auto rotate = [&](auto lo_of, auto hi_of) {
+        // rotate the rotary pairs (f, f + 64) of the lane's key by (cos, sin) at angle index A
+        // (TAB: the lo table entry of the key's row, the hi part is on the query; otherwise the
+        // key's full position, composed from both tables by the angle-addition formulas)
 #pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            __builtin_amdgcn_sched_barrier(0);   // one half at a time: bounds the live table entries
+        for (int s = 0; s < 2; ++s) {
+          __builtin_amdgcn_sched_barrier(0);   // one half at a time: bounds the live table entries
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int f = 32 * s + 8 * gq + dim_of(e);
-              const float2 A = lo_of(8 * s + e, f), Bv = hi_of(f);
-              const float cs = A.x * Bv.x - A.y * Bv.y;
-              const float sn = A.y * Bv.x + A.x * Bv.y;
-              const float x0 = (float)kr[s][e], x1 = (float)kr[s + 2][e];
-              kr[s][e] = (_Float16)fmaf(x0, cs, -x1 * sn);
-              kr[s + 2][e] = (_Float16)fmaf(x0, sn, x1 * cs);
+          for (int e = 0; e < 8; ++e) {
+            float cs, sn;
+            if constexpr (TAB) {
+              cs = lo_q[8 * s + e].x;
+              sn = lo_q[8 * s + e].y;
+            } else {
+              const int f = 32 * s + 8 * lg + dim_of(e);
+              const int pos = (int)((uint32_t)min(k0 + lrow, a.n_kv - 1) % (uint32_t)da.chunk);
+              const float2 A = da.rot_lo[(pos & 63) * half_rot + f], Bv = da.rot_hi[(pos >> 6) * half_rot + f];
+              cs = A.x * Bv.x - A.y * Bv.y;
+              sn = A.y * Bv.x + A.x * Bv.y;
             }
+            const float x0 = (float)kr[s][e], x1 = (float)kr[s + 2][e];
+            kr[s][e] = (_Float16)fmaf(x0, cs, -x1 * sn);
+            kr[s + 2][e] = (_Float16)fmaf(x0, sn, x1 * cs);
           }
-        };
-        if (tab_tile) {
-          const float2* th = (const float2*)(st + kHiRow);
-          rotate([&](int i, int) { return lo_q[i]; }, [&](int f) { return th[f]; });
-        } else {
-          const int64_t pos = (int64_t)min(k0 + lrow, a.n_kv - 1) % da.chunk;
-          const float2* tlo = da.rot_lo + (pos & 63) * half_rot;
-          const float2* thi = da.rot_hi + (pos >> 6) * half_rot;
-          rotate([&](int, int f) { return tlo[f]; }, [&](int f) { return thi[f]; });
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const f16x8 qs = *(const f16x8*)(qsm + lh * 256 + 16 * ((4 * s + lg) ^ lh));
-          sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kr[s], qs, sacc, 0, 0, 0);
-        }
+        for (int s = 0; s < 4; ++s) sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kr[s], qs[s], sacc, 0, 0, 0);
       }
 #pragma unroll
       for (int s = 4; s < 16; ++s) sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kfrag(s), q[s], sacc, 0, 0, 0);
       // C layout: reg e = key 16w + 4 gq + e, column = head hcol
       float sv[4];
-      float mx = -INFINITY;
+      if (k0 >= lo && k0 + kTile - 1 <= hi) {   // whole tile inside [lo, hi]
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int kk = k0 + 16 * w + 4 * gq + e;
-        sv[e] = (kk < lo || kk > hi) ? -INFINITY : sacc[e] * scale_log2;
-        mx = fmaxf(mx, sv[e]);
+        for (int e = 0; e < 4; ++e) sv[e] = sacc[e] * scale_log2;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int kk = k0 + 16 * w + 4 * gq + e;
+          sv[e] = (kk < lo || kk > hi) ? -INFINITY : sacc[e] * scale_log2;
+        }
       }
+      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       if (gq == 0) smax[w][hcol] = mx;
-      __syncthreads();   // also: the transposed scales are complete before the value reads
+      __syncthreads();   // also: the transposed scales are complete before the value reads, and
+                         // every wave has read the rotated query of this tile
+      if constexpr (TAB)
+        if (kt < kt1) rotate_query(qx0, qx1, *(const float4*)(st + kHiRow + 16 * (opaque(tid) & 31)));
+      // every tile holds a key of [lo, hi], so tmax is finite and so is m_used from here on:
+      // masked scores give exp2(-inf) = 0
       const float tmax = fmaxf(fmaxf(smax[0][hcol], smax[1][hcol]), fmaxf(smax[2][hcol], smax[3][hcol]));
       const bool need = tmax > m_used + kTau;
       if (__ballot(need)) {
         const float m_new = need ? tmax : m_used;
-        const float alpha = need ? exp2f(m_used - m_new) : 1.0f;
+        const float alpha = __builtin_amdgcn_exp2f(m_used - m_new);
         l_part *= alpha;
         w_part *= alpha;
 #pragma unroll
@@ -391,7 +443,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
       _Float16 pv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p = sv[e] == -INFINITY ? 0.0f : exp2f(sv[e] - m_used);
+        const float p = __builtin_amdgcn_exp2f(sv[e] - m_used);
         l_part += p;
         pv[e] = (_Float16)p;
         w_part += (float)pv[e];
@@ -400,34 +452,50 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
       __syncthreads();
 
       // ---- O^T += V^T P^T for dims [128w, 128w+128) ------------------------------------------
+      // value operand: transposing reads of rows 32 ks + 8 lg + (lh >> 1), bytes 8 (lh & 1) of a
+      // 16-byte chunk; swizzle key = the row's low 4 bits = 8 (lg & 1) + (lh >> 1).  Value chunk
+      // j = 8 w + dt (q8_0) or 4 w + bb (q4_0) sits at j ^ pv_key: the wave's bits of j and the low
+      // bits of j occupy disjoint bits, so their XORs are taken apart (one term per tile, one per
+      // block).
       // q8_0: o[dt] holds dims 128 w + 16 dt + (4 gq .. +3); q4_0: o[2 bb] and o[2 bb + 1] hold
       // the even and odd dims 128 w + 32 bb + 8 gq + (0, 2, 4, 6) and (1, 3, 5, 7)
+      const int pv_row = 8 * lg + (lh >> 1);
+      const int pv_key = pv_row & 15;
+      const char* vrow =
+          st + pv_row * kRow + 8 * (lh & 1) + 16 * (BITS == 8 ? (8 * w) ^ (pv_key & 8) : (4 * w) ^ (pv_key & 12));
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
+        // operands of the half, all read before any is used
         const f16x8 pb = *(const f16x8*)(pbuf + lh * kTile + 32 * ks + 8 * lg);
+        f16x8 d8[4];
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) d8[bb] = *(const f16x8*)(sT + (4 * w + bb) * kTile + 32 * ks + 8 * lg);
         const char* vr = vrow + 32 * ks * kRow;
+        constexpr int kReads = BITS == 8 ? 8 : 4;
+        v2i cv[kReads];
+#pragma unroll
+        for (int j = 0; j < kReads; ++j)
+          cv[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (lds_v2i*)(lds_char*)(vr + 16 * (j ^ (pv_key & (BITS == 8 ? 7 : 3)))));
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
           // the block's scale goes with the weights: P[h][key] * d[key][4w + bb] for keys
           // 32 ks + 8 gq .. +7 (the values are then the exact integer codes)
-          const f16x8 d8 = *(const f16x8*)(sT + (4 * w + bb) * kTile + 32 * ks + 8 * lg);
-          const f16x8 pd = pb * d8;
+          const f16x8 pd = pb * d8[bb];
           if constexpr (BITS == 8) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
               const int dt = 2 * bb + h;   // chunk 8 w + dt
-              const v2i c = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                  (lds_v2i*)(lds_char*)(vr + 16 * (dt ^ (pv_key & 7))));
-              o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8((uint32_t)c[0], (uint32_t)c[1]), pd, o[dt], 0, 0, 0);
+              o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8((uint32_t)cv[dt][0], (uint32_t)cv[dt][1]), pd,
+                                                             o[dt], 0, 0, 0);
             }
           } else {
             // chunk 4 w + bb = block 4 w + bb: byte i of the chunk holds dims 2 i and 2 i + 1
-            const v2i c = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (lds_v2i*)(lds_char*)(vr + 16 * (bb ^ (pv_key & 3))));
             o[2 * bb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                nibble_col8<false>((uint32_t)c[0], (uint32_t)c[1]), pd, o[2 * bb], 0, 0, 0);
+                nibble_col8<false>((uint32_t)cv[bb][0], (uint32_t)cv[bb][1]), pd, o[2 * bb], 0, 0, 0);
             o[2 * bb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                nibble_col8<true>((uint32_t)c[0], (uint32_t)c[1]), pd, o[2 * bb + 1], 0, 0, 0);
+                nibble_col8<true>((uint32_t)cv[bb][0], (uint32_t)cv[bb][1]), pd, o[2 * bb + 1], 0, 0, 0);
           }
         }
       }
@@ -471,10 +539,14 @@ template <int BITS>
 hipError_t launch_quant(const DecodeArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.base.B * a.base.T;
   if (rows <= 0 || a.n_spans <= 0) return hipSuccess;
-  if (!a.rot_lo || !a.base.rot_f16 || (a.base.n_kv > 0 && (!a.k_scales || !a.base.k_raw)))
+  if (!a.rot_lo || !a.rot_hi || !a.base.rot_f16 || a.chunk <= 0 ||
+      (a.base.n_kv > 0 && (!a.k_scales || !a.base.k_raw)))
     return hipErrorInvalidValue;
   dim3 grid((unsigned)a.n_spans, (unsigned)(rows * a.base.Hkv)), block(256);
-  hipLaunchKernelGGL(attn_decode_quant_kernel<BITS>, grid, block, 0, stream, a);
+  if (a.chunk % 64 == 0 && a.base.Hq <= 8 * a.base.Hkv)
+    hipLaunchKernelGGL((attn_decode_quant_kernel<BITS, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_decode_quant_kernel<BITS, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
