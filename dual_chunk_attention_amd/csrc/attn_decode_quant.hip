@@ -120,6 +120,21 @@ __device__ __forceinline__ f16x8 nibble_col8(uint32_t lo, uint32_t hi) {
   return out;
 }
 
+// max and sum of a value over the four 16-lane rows of the wave (lanes l, l ^ 16, l ^ 32, l ^ 48),
+// by gfx950's row-swapping lane permutes (each swap hands a lane its partner row's value)
+__device__ __forceinline__ float max_over_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // position p of a q4_0 score fragment holds element perm4(p) of its 8 dims
 __device__ __forceinline__ constexpr int perm4(int p) { return 2 * (p & 3) + (p >> 2); }
 
@@ -407,21 +422,21 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
       }
 #pragma unroll
       for (int s = 4; s < 16; ++s) sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kfrag(s), q[s], sacc, 0, 0, 0);
-      // C layout: reg e = key 16w + 4 gq + e, column = head hcol
+      // C layout: reg e = key 16w + 4 gq + e, column = head hcol; sv: raw scores (log2 units once
+      // multiplied by scale_log2 > 0), -inf outside [lo, hi]
       float sv[4];
       if (k0 >= lo && k0 + kTile - 1 <= hi) {   // whole tile inside [lo, hi]
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sv[e] = sacc[e] * scale_log2;
+        for (int e = 0; e < 4; ++e) sv[e] = sacc[e];
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int kk = k0 + 16 * w + 4 * gq + e;
-          sv[e] = (kk < lo || kk > hi) ? -INFINITY : sacc[e] * scale_log2;
+          sv[e] = (kk < lo || kk > hi) ? -INFINITY : sacc[e];
         }
       }
       float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = max_over_rows(mx) * scale_log2;
       if (gq == 0) smax[w][hcol] = mx;
       __syncthreads();   // also: the transposed scales are complete before the value reads, and
                          // every wave has read the rotated query of this tile
@@ -443,7 +458,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
       _Float16 pv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p = __builtin_amdgcn_exp2f(sv[e] - m_used);
+        const float p = __builtin_amdgcn_exp2f(fmaf(sv[e], scale_log2, -m_used));
         l_part += p;
         pv[e] = (_Float16)p;
         w_part += (float)pv[e];
@@ -463,50 +478,48 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
       const int pv_key = pv_row & 15;
       const char* vrow =
           st + pv_row * kRow + 8 * (lh & 1) + 16 * (BITS == 8 ? (8 * w) ^ (pv_key & 8) : (4 * w) ^ (pv_key & 12));
+      // operands of both halves, all read before any is used
+      constexpr int kReads = BITS == 8 ? 8 : 4;
+      f16x8 pb[2], d8[2][4];
+      v2i cv[2][kReads];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        // operands of the half, all read before any is used
-        const f16x8 pb = *(const f16x8*)(pbuf + lh * kTile + 32 * ks + 8 * lg);
-        f16x8 d8[4];
+        pb[ks] = *(const f16x8*)(pbuf + lh * kTile + 32 * ks + 8 * lg);
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) d8[bb] = *(const f16x8*)(sT + (4 * w + bb) * kTile + 32 * ks + 8 * lg);
-        const char* vr = vrow + 32 * ks * kRow;
-        constexpr int kReads = BITS == 8 ? 8 : 4;
-        v2i cv[kReads];
+        for (int bb = 0; bb < 4; ++bb) d8[ks][bb] = *(const f16x8*)(sT + (4 * w + bb) * kTile + 32 * ks + 8 * lg);
 #pragma unroll
         for (int j = 0; j < kReads; ++j)
-          cv[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (lds_v2i*)(lds_char*)(vr + 16 * (j ^ (pv_key & (BITS == 8 ? 7 : 3)))));
-        __builtin_amdgcn_sched_barrier(0);
+          cv[ks][j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (lds_v2i*)(lds_char*)(vrow + 32 * ks * kRow + 16 * (j ^ (pv_key & (BITS == 8 ? 7 : 3)))));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
           // the block's scale goes with the weights: P[h][key] * d[key][4w + bb] for keys
           // 32 ks + 8 gq .. +7 (the values are then the exact integer codes)
-          const f16x8 pd = pb * d8[bb];
+          const f16x8 pd = pb[ks] * d8[ks][bb];
           if constexpr (BITS == 8) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
               const int dt = 2 * bb + h;   // chunk 8 w + dt
-              o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8((uint32_t)cv[dt][0], (uint32_t)cv[dt][1]), pd,
-                                                             o[dt], 0, 0, 0);
+              o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8((uint32_t)cv[ks][dt][0], (uint32_t)cv[ks][dt][1]),
+                                                             pd, o[dt], 0, 0, 0);
             }
           } else {
             // chunk 4 w + bb = block 4 w + bb: byte i of the chunk holds dims 2 i and 2 i + 1
             o[2 * bb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                nibble_col8<false>((uint32_t)cv[bb][0], (uint32_t)cv[bb][1]), pd, o[2 * bb], 0, 0, 0);
+                nibble_col8<false>((uint32_t)cv[ks][bb][0], (uint32_t)cv[ks][bb][1]), pd, o[2 * bb], 0, 0, 0);
             o[2 * bb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                nibble_col8<true>((uint32_t)cv[bb][0], (uint32_t)cv[bb][1]), pd, o[2 * bb + 1], 0, 0, 0);
+                nibble_col8<true>((uint32_t)cv[ks][bb][0], (uint32_t)cv[ks][bb][1]), pd, o[2 * bb + 1], 0, 0, 0);
           }
         }
       }
     }
 
     // ---- combine the row sums of the 4 waves and store the partial ----------------------------
-    float ls = l_part, ws = w_part;
-    ls += __shfl_xor(ls, 16, 64);
-    ls += __shfl_xor(ls, 32, 64);
-    ws += __shfl_xor(ws, 16, 64);
-    ws += __shfl_xor(ws, 32, 64);
+    const float ls = sum_over_rows(l_part), ws = sum_over_rows(w_part);
     if (gq == 0) {
       ssum[w][hcol] = ls;
       wsum[w][hcol] = ws;
