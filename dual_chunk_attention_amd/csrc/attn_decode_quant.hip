@@ -100,12 +100,14 @@ __device__ __forceinline__ f16x8 nibbles8(uint32_t w) {
   return out;
 }
 
-// the low (HIGH = false) or high nibbles of eight bytes (byte i = key i) -> n - 8 as fp16 in key
-// order
+// the low nibbles of eight bytes (byte i = key i) -> n - 8 as fp16 in key order (HIGH = false),
+// or the high nibbles -> 16 (n - 8), taken in place (byte & 0xF0 under the exponent of 1024 is
+// 1024 + 16 n; minus 1152), so that one mask per word does; the caller scales by 1/16 at the end
 template <bool HIGH>
 __device__ __forceinline__ f16x8 nibble_col8(uint32_t lo, uint32_t hi) {
-  const uint32_t a = (HIGH ? lo >> 4 : lo) & 0x0F0F0F0Fu, b = (HIGH ? hi >> 4 : hi) & 0x0F0F0F0Fu;
-  const f16x2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  constexpr uint32_t kMask = HIGH ? 0xF0F0F0F0u : 0x0F0F0F0Fu;
+  const uint32_t a = lo & kMask, b = hi & kMask;
+  const f16x2 off = {(_Float16)(HIGH ? 1152.0f : 1032.0f), (_Float16)(HIGH ? 1152.0f : 1032.0f)};
   f16x2 h[4];
   h[0] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, a, 0x04010400u)) - off;
   h[1] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, a, 0x04030402u)) - off;
@@ -133,6 +135,28 @@ __device__ __forceinline__ float sum_over_rows(float x) {
   x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Rotate the fp16 pair (x0, x1) held in half H of words a and b by (cs, sn), in place:
+// (x0 cs - x1 sn, x0 sn + x1 cs), each product and sum in fp32 and one rounding to fp16 at the
+// end, four mixed-precision fmas per pair (the fp16 operands are read from their halves directly)
+template <int H>
+__device__ __forceinline__ void rot_pair(uint32_t& a, uint32_t& b, float cs, float sn) {
+  float t, u;   // t = -x1 sn, u = x1 cs
+  if constexpr (H == 0)
+    asm("v_fma_mix_f32 %2, %1, -%5, 0 op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mix_f32 %3, %1, %4, 0 op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixlo_f16 %1, %0, %5, %3 op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixlo_f16 %0, %0, %4, %2 op_sel_hi:[1,0,0]"
+        : "+v"(a), "+v"(b), "=&v"(t), "=&v"(u)
+        : "v"(cs), "v"(sn));
+  else
+    asm("v_fma_mix_f32 %2, %1, -%5, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mix_f32 %3, %1, %4, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixhi_f16 %1, %0, %5, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, %0, %4, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "+v"(a), "+v"(b), "=&v"(t), "=&v"(u)
+        : "v"(cs), "v"(sn));
 }
 
 // position p of a q4_0 score fragment holds element perm4(p) of its 8 dims
@@ -392,28 +416,34 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
         f16x8 kr[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) kr[s] = kfrag(s);
-        // rotate the rotary pairs (f, f + 64) of the lane's key by (cos, sin) at angle index A
-        // (TAB: the lo table entry of the key's row, the hi part is on the query; otherwise the
-        // key's full position, composed from both tables by the angle-addition formulas)
+        // rotate the rotary pairs (f, f + 64) of the lane's key by (cos, sin) of its angle (TAB:
+        // the lo table entry of the key's row, the hi part is on the query; otherwise the key's
+        // full position, composed from both tables by the angle-addition formulas)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
           __builtin_amdgcn_sched_barrier(0);   // one half at a time: bounds the live table entries
+          if constexpr (TAB) {
+            struct W4 { uint32_t v[4]; };
+            W4 x0 = __builtin_bit_cast(W4, kr[s]), x1 = __builtin_bit_cast(W4, kr[s + 2]);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            float cs, sn;
-            if constexpr (TAB) {
-              cs = lo_q[8 * s + e].x;
-              sn = lo_q[8 * s + e].y;
-            } else {
+            for (int j = 0; j < 4; ++j) {
+              rot_pair<0>(x0.v[j], x1.v[j], lo_q[8 * s + 2 * j].x, lo_q[8 * s + 2 * j].y);
+              rot_pair<1>(x0.v[j], x1.v[j], lo_q[8 * s + 2 * j + 1].x, lo_q[8 * s + 2 * j + 1].y);
+            }
+            kr[s] = __builtin_bit_cast(f16x8, x0);
+            kr[s + 2] = __builtin_bit_cast(f16x8, x1);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
               const int f = 32 * s + 8 * lg + dim_of(e);
               const int pos = (int)((uint32_t)min(k0 + lrow, a.n_kv - 1) % (uint32_t)da.chunk);
               const float2 A = da.rot_lo[(pos & 63) * half_rot + f], Bv = da.rot_hi[(pos >> 6) * half_rot + f];
-              cs = A.x * Bv.x - A.y * Bv.y;
-              sn = A.y * Bv.x + A.x * Bv.y;
+              const float cs = A.x * Bv.x - A.y * Bv.y;
+              const float sn = A.y * Bv.x + A.x * Bv.y;
+              const float x0 = (float)kr[s][e], x1 = (float)kr[s + 2][e];
+              kr[s][e] = (_Float16)fmaf(x0, cs, -x1 * sn);
+              kr[s + 2][e] = (_Float16)fmaf(x0, sn, x1 * cs);
             }
-            const float x0 = (float)kr[s][e], x1 = (float)kr[s + 2][e];
-            kr[s][e] = (_Float16)fmaf(x0, cs, -x1 * sn);
-            kr[s + 2][e] = (_Float16)fmaf(x0, sn, x1 * cs);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -473,7 +503,8 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
       // bits of j occupy disjoint bits, so their XORs are taken apart (one term per tile, one per
       // block).
       // q8_0: o[dt] holds dims 128 w + 16 dt + (4 gq .. +3); q4_0: o[2 bb] and o[2 bb + 1] hold
-      // the even and odd dims 128 w + 32 bb + 8 gq + (0, 2, 4, 6) and (1, 3, 5, 7)
+      // the even and odd dims 128 w + 32 bb + 8 gq + (0, 2, 4, 6) and (1, 3, 5, 7), the odd ones
+      // times 16
       const int pv_row = 8 * lg + (lh >> 1);
       const int pv_key = pv_row & 15;
       const char* vrow =
@@ -537,7 +568,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
       } else {
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
-          const f32x4 ev = o[2 * bb] * inv, od = o[2 * bb + 1] * inv;
+          const f32x4 ev = o[2 * bb] * inv, od = o[2 * bb + 1] * (inv * 0.0625f);   // odd dims: 16x
           *(f32x4*)(orow + 32 * bb + 8 * gq) = f32x4{ev[0], od[0], ev[1], od[1]};
           *(f32x4*)(orow + 32 * bb + 8 * gq + 4) = f32x4{ev[2], od[2], ev[3], od[3]};
         }
