@@ -36,6 +36,7 @@ constexpr int kD = 512;
 constexpr int kTile = 64;
 constexpr int kScaleBytes = kTile * kD / 32 * 2;  // 2 KiB of fp16 scales per tile, [key][block]
 constexpr float kTau = 8.0f;
+constexpr int kPad = kTile + 8;   // row stride (halves) of the weight and transposed-scale buffers
 
 // stage layout per code width: codes [64 rows][kRow bytes], scales, the tile's hi table row
 template <int BITS>
@@ -183,8 +184,9 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
   constexpr int kHiRow = LY::kHiRow, kRpl = LY::kRowsPerLoad;
   const AttnArgs& a = da.base;
   __shared__ __attribute__((aligned(1024))) char stage[2 * kStageBytes];
-  __shared__ __attribute__((aligned(16))) _Float16 pbuf[16 * kTile];   // P[head][key]
-  __shared__ __attribute__((aligned(16))) _Float16 sT[16 * kTile];     // tile scales, [block][key]
+  // P[head][key] and the tile's scales [block][key], rows padded to kPad halves (bank spread)
+  __shared__ __attribute__((aligned(16))) _Float16 pbuf[16 * kPad];
+  __shared__ __attribute__((aligned(16))) _Float16 sT[16 * kPad];
   __shared__ __attribute__((aligned(16))) char qsm[16 * 256];          // rotated query dims, fp16
   __shared__ float smax[4][16], ssum[4][16], wsum[4][16];
 
@@ -395,11 +397,11 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
       for (int s = 0; s < 4; ++s) qs[s] = *(const f16x8*)(qsm + lh * 256 + 16 * ((4 * s + lg) ^ lh));
       __builtin_amdgcn_sched_barrier(0);
       {
-        uint16_t* t = (uint16_t*)sT + 4 * lg * kTile + lrow;
-        t[0 * kTile] = (uint16_t)d4.x;
-        t[1 * kTile] = (uint16_t)(d4.x >> 16);
-        t[2 * kTile] = (uint16_t)d4.y;
-        t[3 * kTile] = (uint16_t)(d4.y >> 16);
+        uint16_t* t = (uint16_t*)sT + 4 * lg * kPad + lrow;
+        t[0 * kPad] = (uint16_t)d4.x;
+        t[1 * kPad] = (uint16_t)(d4.x >> 16);
+        t[2 * kPad] = (uint16_t)d4.y;
+        t[3 * kPad] = (uint16_t)(d4.y >> 16);
       }
 
       // ---- S^T for keys [16w, 16w+16): codes -> fp16 d*q in registers ------------------------
@@ -493,7 +495,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
         pv[e] = (_Float16)p;
         w_part += (float)pv[e];
       }
-      *(uint2*)(pbuf + lh * kTile + 16 * w + 4 * lg) = __builtin_bit_cast(uint2, pv);
+      *(uint2*)(pbuf + lh * kPad + 16 * w + 4 * lg) = __builtin_bit_cast(uint2, pv);
       __syncthreads();
 
       // ---- O^T += V^T P^T for dims [128w, 128w+128) ------------------------------------------
@@ -515,9 +517,9 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
       v2i cv[2][kReads];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        pb[ks] = *(const f16x8*)(pbuf + lh * kTile + 32 * ks + 8 * lg);
+        pb[ks] = *(const f16x8*)(pbuf + lh * kPad + 32 * ks + 8 * lg);
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) d8[ks][bb] = *(const f16x8*)(sT + (4 * w + bb) * kTile + 32 * ks + 8 * lg);
+        for (int bb = 0; bb < 4; ++bb) d8[ks][bb] = *(const f16x8*)(sT + (4 * w + bb) * kPad + 32 * ks + 8 * lg);
 #pragma unroll
         for (int j = 0; j < kReads; ++j)
           cv[ks][j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
