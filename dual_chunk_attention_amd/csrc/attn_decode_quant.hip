@@ -310,9 +310,10 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
 
     // tile k0..k0+63 by direct global->LDS loads into stage buf: wave w the code rows
     // 16w..16w+15 (kRpl rows of kRow bytes per load; position p of row r receives global chunk
-    // p ^ (r & 15)), waves 0 and 1 the scale rows 0..31 and 32..63 (lane l the half l%2 of row
-    // l/2), lanes 0..31 of wave 2 (TAB) the hi table row of the tile after it; rows outside the
-    // region re-read its first or last cell (their scores are masked)
+    // p ^ (r & 15)), waves 0 and 1 the scale rows 0..31 and 32..63 (lane l the slot l%2 of row
+    // r = l/2, which receives the row's half (l%2) ^ bit 3 of r), lanes 0..31 of wave 2 (TAB) the
+    // hi table row of the tile after it; rows outside the region re-read its first or last cell
+    // (their scores are masked)
     auto issue = [&](int buf, int k0, int hr_next) {
       const uint32_t base = stage_lds + buf * kStageBytes;
       const int ln = opaque(l);
@@ -343,7 +344,9 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
         const char* sb = uniform_ptr((const char*)scales_b + (int64_t)(k0 - da.key0) * key_sbytes);
         // (not nontemporal: the scale rows of the KV heads share cache lines, which the other
         // head's workgroup reads as well)
-        dma16_off(sb, __umul24((uint32_t)min(max(row, first), last), key_sbytes) + 16 * (ln & 1),
+        // LDS slot (row, half) receives the row's global half ^ bit 3 of the row, so that the
+        // 16-row reads of one half spread over all banks
+        dma16_off(sb, __umul24((uint32_t)min(max(row, first), last), key_sbytes) + 16 * ((ln & 1) ^ ((row >> 3) & 1)),
                   base + kCodeBytes + wu * 1024);
       }
       if (TAB && wu == 2 && ln < 32)   // hi row of the next tile (512 bytes: lanes 0..31)
@@ -374,9 +377,10 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
       // 32 s + 8 lg .. +7 for k-step s) and scales, the rotated query, the transposed scales' source
       const char* krow = st + lrow * kRow;
       f16x8 dsc[2];
-      dsc[0] = *(const f16x8*)(st + kCodeBytes + lrow * 32);
-      dsc[1] = *(const f16x8*)(st + kCodeBytes + lrow * 32 + 16);
-      const uint2 d4 = *(const uint2*)(st + kCodeBytes + lrow * 32 + 8 * lg);   // blocks 4lg..+3
+      const int sh = 16 * ((lrow >> 3) & 1);   // the scale rows' half swizzle
+      dsc[0] = *(const f16x8*)(st + kCodeBytes + lrow * 32 + sh);
+      dsc[1] = *(const f16x8*)(st + kCodeBytes + lrow * 32 + (sh ^ 16));
+      const uint2 d4 = *(const uint2*)(st + kCodeBytes + lrow * 32 + ((16 * (lg >> 1)) ^ sh) + 8 * (lg & 1));   // blocks 4lg..+3
       uint2 cw[16];   // q8_0: 8 codes; q4_0: 8 codes in .x
       if constexpr (BITS == 8) {
         // chunk (2 s + (lg >> 1)) ^ lh, bytes 8 (lg & 1): with s = 8 t + u that is byte
