@@ -81,17 +81,18 @@ __device__ __forceinline__ f16x8 codes8(uint32_t lo, uint32_t hi) {
 }
 #pragma clang diagnostic pop
 
-// eight 4-bit codes of one word (element e at bits 4e..4e+3) -> n - 8 as fp16, in the order
-// (0, 2, 4, 6, 1, 3, 5, 7): the low nibbles of the four bytes are the even elements, the high
-// nibbles the odd ones; each byte pair goes under the fp16 exponent of 1024 by one byte permute
+// eight 4-bit codes of one word (element e at bits 4e..4e+3) -> fp16 in the order
+// (0, 2, 4, 6, 1, 3, 5, 7): the low nibbles of the four bytes are the even elements, n - 8; the
+// high nibbles the odd ones, taken in place as 16 (n - 8) (byte & 0xF0 under the exponent of 1024
+// is 1024 + 16 n; minus 1152); each byte pair goes under the exponent by one byte permute
 __device__ __forceinline__ f16x8 nibbles8(uint32_t w) {
-  const uint32_t ev = w & 0x0F0F0F0Fu, od = (w >> 4) & 0x0F0F0F0Fu;
-  const f16x2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const uint32_t ev = w & 0x0F0F0F0Fu, od = w & 0xF0F0F0F0u;
+  const f16x2 off = {(_Float16)1032.0f, (_Float16)1032.0f}, off16 = {(_Float16)1152.0f, (_Float16)1152.0f};
   f16x2 h[4];
   h[0] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, ev, 0x04010400u)) - off;
   h[1] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, ev, 0x04030402u)) - off;
-  h[2] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, od, 0x04010400u)) - off;
-  h[3] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, od, 0x04030402u)) - off;
+  h[2] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, od, 0x04010400u)) - off16;
+  h[3] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, od, 0x04030402u)) - off16;
   f16x8 out;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -371,7 +372,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
       // lane-dependent offsets, recomputed per tile
       const int ln = opaque(l);
       const int lh = ln & 15, lg = ln >> 4;
-      const int lrow = 16 * w + lh;
+      const int lrow = 16 * wu + lh;
 
       // ---- score operands, all read before any is used: the lane's key row of codes (dims
       // 32 s + 8 lg .. +7 for k-step s) and scales, the rotated query, the transposed scales' source
@@ -409,13 +410,25 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
       }
 
       // ---- S^T for keys [16w, 16w+16): codes -> fp16 d*q in registers ------------------------
+      // q4_0: the odd elements come as 16 (n - 8) and take d / 16 (exact for d >= 2^-10; below,
+      // d / 16 is subnormal and the element's absolute error stays under 2^-25 * 128)
+      f16x8 dsc16[2];
+      if constexpr (BITS == 4) {
+        const f16x8 r16 = {(_Float16)0.0625f, (_Float16)0.0625f, (_Float16)0.0625f, (_Float16)0.0625f,
+                           (_Float16)0.0625f, (_Float16)0.0625f, (_Float16)0.0625f, (_Float16)0.0625f};
+        dsc16[0] = dsc[0] * r16;
+        dsc16[1] = dsc[1] * r16;
+      }
       auto kfrag = [&](int s) {
         const _Float16 d = dsc[s >> 3][s & 7];
-        const f16x8 dd = {d, d, d, d, d, d, d, d};
-        if constexpr (BITS == 8)
+        if constexpr (BITS == 8) {
+          const f16x8 dd = {d, d, d, d, d, d, d, d};
           return codes8(cw[s].x, cw[s].y) * dd;
-        else
+        } else {
+          const _Float16 d16 = dsc16[s >> 3][s & 7];
+          const f16x8 dd = {d, d, d, d, d16, d16, d16, d16};
           return nibbles8(cw[s].x) * dd;
+        }
       };
       f32x4 sacc = f32x4{};
       {
@@ -467,7 +480,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int kk = k0 + 16 * w + 4 * gq + e;
+          const int kk = k0 + 16 * wu + 4 * gq + e;
           sv[e] = (kk < lo || kk > hi) ? -INFINITY : sacc[e];
         }
       }
@@ -491,15 +504,17 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
         for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
         m_used = m_new;
       }
-      _Float16 pv[4];
+      float p[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sv[e], scale_log2, -m_used));
-        l_part += p;
-        pv[e] = (_Float16)p;
-        w_part += (float)pv[e];
+        p[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], scale_log2, -m_used));
+        l_part += p[e];
       }
-      *(uint2*)(pbuf + lh * kPad + 16 * w + 4 * lg) = __builtin_bit_cast(uint2, pv);
+      // the fp16 weights, packed in pairs; their sum (exact in fp32) by a dot with (1, 1)
+      const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+      const f16x2 pv01 = {(_Float16)p[0], (_Float16)p[1]}, pv23 = {(_Float16)p[2], (_Float16)p[3]};
+      w_part = __builtin_amdgcn_fdot2(pv23, one2, __builtin_amdgcn_fdot2(pv01, one2, w_part, false), false);
+      *(uint2*)(pbuf + lh * kPad + 16 * wu + 4 * lg) = uint2{__builtin_bit_cast(uint32_t, pv01), __builtin_bit_cast(uint32_t, pv23)};
       __syncthreads();
 
       // ---- O^T += V^T P^T for dims [128w, 128w+128) ------------------------------------------
@@ -514,7 +529,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
       const int pv_row = 8 * lg + (lh >> 1);
       const int pv_key = pv_row & 15;
       const char* vrow =
-          st + pv_row * kRow + 8 * (lh & 1) + 16 * (BITS == 8 ? (8 * w) ^ (pv_key & 8) : (4 * w) ^ (pv_key & 12));
+          st + pv_row * kRow + 8 * (lh & 1) + 16 * (BITS == 8 ? (8 * wu) ^ (pv_key & 8) : (4 * wu) ^ (pv_key & 12));
       // operands of both halves, all read before any is used
       constexpr int kReads = BITS == 8 ? 8 : 4;
       f16x8 pb[2], d8[2][4];
@@ -523,7 +538,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
       for (int ks = 0; ks < 2; ++ks) {
         pb[ks] = *(const f16x8*)(pbuf + lh * kPad + 32 * ks + 8 * lg);
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) d8[ks][bb] = *(const f16x8*)(sT + (4 * w + bb) * kPad + 32 * ks + 8 * lg);
+        for (int bb = 0; bb < 4; ++bb) d8[ks][bb] = *(const f16x8*)(sT + (4 * wu + bb) * kPad + 32 * ks + 8 * lg);
 #pragma unroll
         for (int j = 0; j < kReads; ++j)
           cv[ks][j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
