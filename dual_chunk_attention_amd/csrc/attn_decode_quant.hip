@@ -21,10 +21,17 @@
 //    loads pick the global chunk that belongs at each position), so that both the 16-row score
 //    reads and the 8-row transposing reads hit 16 distinct chunk slots.
 //  * The rotary dims of a key are rotated in registers at j mod c from the fp64-built cos/sin
-//    tables (lo[p & 63] composed with hi[p >> 6]), as in the bf16 passes.
+//    tables, lo[p & 63] and hi[p >> 6] by angle addition.  With c a multiple of 64 (and at most 8
+//    query heads per KV head: the TAB form) a 64-key tile sits at p0 + row under one hi row, and
+//    <q, R(hi + lo) k> = <R(-hi) q, R(lo) k>: the workgroup turns the query's rotary pairs by
+//    minus the tile's hi angles once per tile, and each key takes only its row's lo entry, which
+//    the lane keeps in registers.  Otherwise each key composes both tables (the general form).
 //  * Codes to fp16, exactly: an int8 code by one sign-extending conversion; a 4-bit code n by
 //    placing it under the fp16 exponent of 1024 (bit pattern 0x6400 | n = 1024 + n) and
-//    subtracting 1032.  One fp16 multiply by d then gives the value (one rounding).
+//    subtracting 1032, or, for a high nibble taken in place, 1024 + 16 n minus 1152 = 16 (n - 8)
+//    with the scale divided by 16.  One fp16 multiply by d then gives the value (one rounding).
+//  * The operands of each product are read from LDS together, before the first use, so that the
+//    MFMAs do not wait out one LDS round trip each.
 //  * q4_0 score fragments hold their 8 dims in the order the nibble extraction yields,
 //    (0, 2, 4, 6, 1, 3, 5, 7); the query fragments are stored in the same order.
 #include "common.h"
