@@ -26,10 +26,15 @@
 //    <q, R(hi + lo) k> = <R(-hi) q, R(lo) k>: the workgroup turns the query's rotary pairs by
 //    minus the tile's hi angles once per tile, and each key takes only its row's lo entry, which
 //    the lane keeps in registers.  Otherwise each key composes both tables (the general form).
-//  * Codes to fp16, exactly: an int8 code by one sign-extending conversion; a 4-bit code n by
-//    placing it under the fp16 exponent of 1024 (bit pattern 0x6400 | n = 1024 + n) and
+//  * Score codes to fp16, exactly: an int8 code by one sign-extending conversion; a 4-bit code n
+//    by placing it under the fp16 exponent of 1024 (bit pattern 0x6400 | n = 1024 + n) and
 //    subtracting 1032, or, for a high nibble taken in place, 1024 + 16 n minus 1152 = 16 (n - 8)
 //    with the scale divided by 16.  One fp16 multiply by d then gives the value (one rounding).
+//  * Value codes need no arithmetic: a byte under a zero high byte is the fp16 subnormal
+//    byte * 2^-24, exact (q8_0: code ^ 0x80 = code + 128; q4_0: the low nibble n, the high nibble
+//    in place as 16 n); the products with the weights are exact in the fp32 accumulators, and
+//    the offset (128 or 8) comes back out at the end from the sum of the weights times the
+//    scales, which one more MFMA per block accumulates against a ones operand.
 //  * The operands of each product are read from LDS together, before the first use, so that the
 //    MFMAs do not wait out one LDS round trip each.
 //  * q4_0 score fragments hold their 8 dims in the order the nibble extraction yields,
@@ -109,26 +114,14 @@ __device__ __forceinline__ f16x8 nibbles8(uint32_t w) {
   return out;
 }
 
-// the low nibbles of eight bytes (byte i = key i) -> n - 8 as fp16 in key order (HIGH = false),
-// or the high nibbles -> 16 (n - 8), taken in place (byte & 0xF0 under the exponent of 1024 is
-// 1024 + 16 n; minus 1152), so that one mask per word does; the caller scales by 1/16 at the end
-template <bool HIGH>
-__device__ __forceinline__ f16x8 nibble_col8(uint32_t lo, uint32_t hi) {
-  constexpr uint32_t kMask = HIGH ? 0xF0F0F0F0u : 0x0F0F0F0Fu;
-  const uint32_t a = lo & kMask, b = hi & kMask;
-  const f16x2 off = {(_Float16)(HIGH ? 1152.0f : 1032.0f), (_Float16)(HIGH ? 1152.0f : 1032.0f)};
-  f16x2 h[4];
-  h[0] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, a, 0x04010400u)) - off;
-  h[1] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, a, 0x04030402u)) - off;
-  h[2] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, b, 0x04010400u)) - off;
-  h[3] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, b, 0x04030402u)) - off;
-  f16x8 out;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    out[2 * i] = h[i][0];
-    out[2 * i + 1] = h[i][1];
-  }
-  return out;
+// eight bytes (two words, byte i = element i) -> fp16 subnormals byte * 2^-24, exactly: each byte
+// goes under a zero high byte by one byte permute per pair.  The value product takes its codes in
+// this form (q8_0: code + 128; q4_0: n, or 16 n for a high nibble masked in place) and removes the
+// offset at the end from the sum of its weights (see the value product)
+__device__ __forceinline__ f16x8 bytes_sub8(uint32_t a, uint32_t b) {
+  const uint32_t h[4] = {__builtin_amdgcn_perm(0u, a, 0x0C010C00u), __builtin_amdgcn_perm(0u, a, 0x0C030C02u),
+                         __builtin_amdgcn_perm(0u, b, 0x0C010C00u), __builtin_amdgcn_perm(0u, b, 0x0C030C02u)};
+  return __builtin_bit_cast(f16x8, h);
 }
 
 // max and sum of a value over the four 16-lane rows of the wave (lanes l, l ^ 16, l ^ 32, l ^ 48),
@@ -312,6 +305,11 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
     f32x4 o[8];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{};
+    // wsb[bb]: per head, the sum over keys of the weight times the key's scale of block 4 w + bb
+    // (every row of the 16x16 tile the same), which takes the codes' offset out of O at the end
+    f32x4 wsb[4];
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) wsb[bb] = f32x4{};
     // l_part: exact row sum (LSE); w_part: sum of the fp16 weights the PV product uses (O's
     // normaliser, so that weights and normaliser agree)
     float m_used = -INFINITY, l_part = 0.0f, w_part = 0.0f;
@@ -509,6 +507,8 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
         w_part *= alpha;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) wsb[bb] *= alpha;
         m_used = m_new;
       }
       float p[4];
@@ -552,26 +552,34 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
               (lds_v2i*)(lds_char*)(vrow + 32 * ks * kRow + 16 * (j ^ (pv_key & (BITS == 8 ? 7 : 3)))));
       }
       __builtin_amdgcn_sched_barrier(0);
+      const f16x8 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f,
+                          (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
           // the block's scale goes with the weights: P[h][key] * d[key][4w + bb] for keys
-          // 32 ks + 8 gq .. +7 (the values are then the exact integer codes)
+          // 32 ks + 8 gq .. +7; the codes enter as subnormals (code + offset) * 2^-24, so
+          // O = 2^24 sum_keys (code + offset) 2^-24 p d - offset * sum_keys p d, the second sum
+          // taken by one more product against ones
           const f16x8 pd = pb[ks] * d8[ks][bb];
+          wsb[bb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pd, wsb[bb], 0, 0, 0);
           if constexpr (BITS == 8) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-              const int dt = 2 * bb + h;   // chunk 8 w + dt
-              o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8((uint32_t)cv[ks][dt][0], (uint32_t)cv[ks][dt][1]),
-                                                             pd, o[dt], 0, 0, 0);
+              const int dt = 2 * bb + h;   // chunk 8 w + dt; byte ^ 0x80 = code + 128
+              o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                  bytes_sub8((uint32_t)cv[ks][dt][0] ^ 0x80808080u, (uint32_t)cv[ks][dt][1] ^ 0x80808080u), pd, o[dt],
+                  0, 0, 0);
             }
           } else {
-            // chunk 4 w + bb = block 4 w + bb: byte i of the chunk holds dims 2 i and 2 i + 1
+            // chunk 4 w + bb = block 4 w + bb: byte i of the chunk holds dims 2 i (low nibble, n)
+            // and 2 i + 1 (high nibble, taken in place as 16 n)
+            const uint32_t c0 = (uint32_t)cv[ks][bb][0], c1 = (uint32_t)cv[ks][bb][1];
             o[2 * bb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                nibble_col8<false>((uint32_t)cv[ks][bb][0], (uint32_t)cv[ks][bb][1]), pd, o[2 * bb], 0, 0, 0);
+                bytes_sub8(c0 & 0x0F0F0F0Fu, c1 & 0x0F0F0F0Fu), pd, o[2 * bb], 0, 0, 0);
             o[2 * bb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                nibble_col8<true>((uint32_t)cv[ks][bb][0], (uint32_t)cv[ks][bb][1]), pd, o[2 * bb + 1], 0, 0, 0);
+                bytes_sub8(c0 & 0xF0F0F0F0u, c1 & 0xF0F0F0F0u), pd, o[2 * bb + 1], 0, 0, 0);
           }
         }
       }
@@ -590,13 +598,16 @@ __global__ __launch_bounds__(256, 2) void attn_decode_quant_kernel(DecodeArgs da
     const float inv = nonempty ? 1.0f / w_tot : 0.0f;
     if (head_ok) {
       float* orow = da.o_part + ((int64_t)slot * rows * a.Hq + rowhead) * kD + 128 * w;
+      // O = (2^24 o - offset * wsb) / w: the scaling by 2^24 (2^20 for the high nibbles) is exact
+      constexpr float k24 = 16777216.0f, k20 = 1048576.0f;
       if constexpr (BITS == 8) {
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) *(f32x4*)(orow + 16 * dt + 4 * gq) = o[dt] * inv;
+        for (int dt = 0; dt < 8; ++dt)
+          *(f32x4*)(orow + 16 * dt + 4 * gq) = (o[dt] * k24 - wsb[dt >> 1] * 128.0f) * inv;
       } else {
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
-          const f32x4 ev = o[2 * bb] * inv, od = o[2 * bb + 1] * (inv * 0.0625f);   // odd dims: 16x
+          const f32x4 ev = (o[2 * bb] * k24 - wsb[bb] * 8.0f) * inv, od = (o[2 * bb + 1] * k20 - wsb[bb] * 8.0f) * inv;
           *(f32x4*)(orow + 32 * bb + 8 * gq) = f32x4{ev[0], od[0], ev[1], od[1]};
           *(f32x4*)(orow + 32 * bb + 8 * gq + 4) = f32x4{ev[2], od[2], ev[3], od[3]};
         }
