@@ -22,12 +22,14 @@
 //    tile's keys are formed between the O^T MFMAs of its first half.
 //  * The key tiles of the three regimes form one sequence (intra, succ, inter); at a regime change
 //    only the rotary Q fragments are reloaded.
-//  * Reference maximum per row: the first tile with a valid key sets it, and exp2 arguments stay
-//    <= 64 (log2 units) while no tile exceeds it by more than that.  A tile that does (rare) raises
-//    a flag of the workgroup; after its tile sequence a flagged workgroup runs the sequence twice
-//    more: once with each row's reference following every tile's maximum (its exponents stay <= 0;
-//    its O is discarded), which leaves the exact row maxima, and once more in full against them.
-//    O never leaves the registers before the end, and the pass needs no scratch memory.
+//  * Reference maximum per row: the first tile with a valid key sets it; later tiles take no row
+//    maximum at all.  The pass keeps its result while every row's sums of p stay below 2^80 (then
+//    every exponent stayed below 80 and O is far from overflow; the arithmetic is that of any
+//    other reference).  A pass whose sums do not (rare; an inf or NaN included) raises a flag of
+//    the workgroup; after its tile sequence a flagged workgroup runs the sequence twice more: once
+//    with each row's reference following every tile's maximum (its exponents stay <= 0; its O is
+//    discarded), which leaves the exact row maxima, and once more in full against them.  O never
+//    leaves the registers before the end, and the pass needs no scratch memory.
 //  * Workgroups are launched latest query block first (longest causal work first).
 #include <type_traits>
 
@@ -43,7 +45,7 @@ constexpr int kRawBytes = kNK * kD * 2;          // 32 KiB: raw dims 0..511, 1 K
 constexpr int kRotBytes = kNK * kRot * 2;        // 8 KiB: rotated dims 0..127, 256-byte rows
 constexpr int kStageBytes = kRawBytes + kRotBytes;
 constexpr int kStages = 3;
-constexpr float kTau = 64.0f;                    // reference-move threshold (log2 units)
+constexpr float kSumMax = 0x1p80f;               // bound on a row's sums of p in pass 0
 constexpr int kDepthK = 4;                       // K fragments in flight ahead of their MFMA
 constexpr int kDepthV = 3;                       // V^T fragments in flight ahead of their MFMA
 
@@ -261,8 +263,9 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
   // ahead of their MFMA behind scheduling fences; the ten load parts of tile dma_k0 into the
   // stage at dma_off go out with MFMA pairs 1, 2, 4, 5, ..., 13, 14 (`inside`: that tile lies
   // wholly inside the cache, so the loads sit in the pairs' asm and take the precomputed lane
-  // offsets; otherwise they follow the pairs in their general, clamped form) ----------------
-  auto scores = [&](auto inside, int stg_off, int dma_off, int dma_k0) {
+  // offsets; otherwise they follow the pairs in their general, clamped form); `hook(p)` runs
+  // after pair p, inside its fence ---------------------------------------------------------------
+  auto scores = [&](auto inside, int stg_off, int dma_off, int dma_k0, auto&& hook) {
     const char* raw = smem + stg_off + n * 1024;
     const char* rot = smem + stg_off + kRawBytes + n * 256;
     f32x16 acc;
@@ -293,6 +296,7 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
         kf[(s + 1) % kDepthK] = kld(s + 1 + kDepthK);
       }
       if (!decltype(inside)::value && p % 3 != 0) issue_part(dma_off, dma_k0, j);
+      hook(p);
       __builtin_amdgcn_sched_barrier(0);
     }
     // the VALU reads the result next: wait out the last MFMA's passes
@@ -322,7 +326,8 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
 
   // p = exp2(s * scale_log2 - m) for scores e, e+1 into pk: a masked score (-inf) gives 0; a row
   // without any valid key so far has m = -inf and only masked scores, so any finite reference gives
-  // the same zeros.  The exponents are <= kTau, so the raw v_exp_f32 suffices.  psum: the exact p;
+  // the same zeros.  An exponent above 128 gives inf, which the end-of-pass check of the sums
+  // catches, so the raw v_exp_f32 suffices.  psum: the exact p;
   // wsum: the bf16-rounded p that the PV product uses (exact products by one).
   // Sums go to partial accumulators (psum[e/2 % 4], wsum[e/2 % 2]) so that the adds do not form
   // one long dependent chain (one wave per SIMD exposes every VALU latency).
@@ -337,10 +342,9 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
     pk[e >> 3][(e & 7) + 1] = pb[1];
   };
 
-  // The scores of tile i (raw, in sv): mask to each row's interval, row maximum, reference of the
-  // row (the first tile with a valid key sets it, O of the row being still 0; a tile more than
-  // kTau above it raises the workgroup's flag), and the probabilities of keys 0..15 of the tile
-  // (pk[0]).
+  // The scores of tile i (raw, in sv): mask to each row's interval, reference of the row (the
+  // first tile with a valid key sets it from its row maximum, O of the row being still 0), and the
+  // probabilities of keys 0..15 of the tile (pk[0]).
   auto softmax_head = [&](float* sv, int i, bf16x8* pk, float& neg_m, float* psum, float* wsum) {
     const int k0 = k0_of(i);
     if (!(sel(i, full_lo[0], full_lo[1], full_lo[2]) <= k0 &&
@@ -353,18 +357,18 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
         if (kk < lo_eff || kk > hi_eff) sv[e] = -INFINITY;
       }
     }
-    // row maximum as a tree (depth 3 of 3-input maxima)
-    float m6[6];
+    // the row maximum (a tree of 3-input maxima and the exchange with the row's other half), only
+    // while some row of the wave has no reference yet, and in pass 1
+    if (pass == 1 || __ballot(m_used == -INFINITY) != 0) {
+      float m6[6];
 #pragma unroll
-    for (int k = 0; k < 5; ++k) m6[k] = fmaxf(fmaxf(sv[3 * k], sv[3 * k + 1]), sv[3 * k + 2]);
-    m6[5] = sv[15];
-    float mx = fmaxf(fmaxf(fmaxf(m6[0], m6[1]), m6[2]), fmaxf(fmaxf(m6[3], m6[4]), m6[5]));
-    {
+      for (int k = 0; k < 5; ++k) m6[k] = fmaxf(fmaxf(sv[3 * k], sv[3 * k + 1]), sv[3 * k + 2]);
+      m6[5] = sv[15];
+      float mx = fmaxf(fmaxf(fmaxf(m6[0], m6[1]), m6[2]), fmaxf(fmaxf(m6[3], m6[4]), m6[5]));
       auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       mx = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1])) * scale_log2;
+      m_used = (pass == 1 || m_used == -INFINITY) ? fmaxf(m_used, mx) : m_used;
     }
-    m_used = (pass == 1 || m_used == -INFINITY) ? fmaxf(m_used, mx) : m_used;
-    if (pass == 0 && __ballot(mx > m_used + kTau) != 0 && l == 0) s_flag = 1;
     neg_m = m_used == -INFINITY ? 0.0f : -m_used;
 #pragma unroll
     for (int k = 0; k < 4; ++k) psum[k] = 0.0f;
@@ -421,16 +425,21 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
       // scores of tile i, with the loads of tile i+2 (past the end: the last tile again, into a
       // stage no longer read, which keeps ten loads per wave and tile in flight)
       const int dk0 = k0_of(min(i + 2, n_tiles - 1));
-      const f32x16 acc = a.n_kv - 1 - dk0 >= kNK - 1 ? scores(std::true_type{}, off_c, off_d, dk0)
-                                                     : scores(std::false_type{}, off_c, off_d, dk0);
+      // the first V^T fragments of the tile go out with the last two score pairs (their LDS
+      // latency then hides under those MFMAs and the softmax)
+      bf16x8 vf[kDepthV];
+      auto hook = [&](int p) {
+        if (p == 14) {
+          vf[0] = vload(off_c, 0);
+          vf[1] = vload(off_c, 1);
+        }
+        if (p == 15) vf[2] = vload(off_c, 2);
+      };
+      const f32x16 acc = a.n_kv - 1 - dk0 >= kNK - 1 ? scores(std::true_type{}, off_c, off_d, dk0, hook)
+                                                     : scores(std::false_type{}, off_c, off_d, dk0, hook);
       float sv[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) sv[e] = acc[e];
-      // the first V^T fragments of the tile go out before the softmax, whose VALU work hides their
-      // LDS latency
-      bf16x8 vf[kDepthV];
-#pragma unroll
-      for (int j = 0; j < kDepthV; ++j) vf[j] = vload(off_c, j);
       bf16x8 pk[2];
       float neg_m, psum[4], wsum[2];
       softmax_head(sv, i, pk, neg_m, psum, wsum);
@@ -446,6 +455,9 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
       off_n = off_d;
       off_d = t_off;
     }
+    // pass 0 keeps its result while every row's sums of p stay below kSumMax; otherwise (an inf
+    // or NaN included) the workgroup raises its flag
+    if (pass == 0 && __ballot(!(l_part < kSumMax && w_part < kSumMax)) != 0 && l == 0) s_flag = 1;
     // every wave's flag write and tile loads are complete; the stages may be reloaded
     wait_vm0();
     __syncthreads();
