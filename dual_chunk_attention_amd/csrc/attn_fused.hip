@@ -476,30 +476,59 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
   }
   const bool nonempty = l_tot > 0.0f && w_tot > 0.0f;
   const float inv = nonempty ? 1.0f / w_tot : 0.0f;
-  if (row_valid) {
+  // O leaves through LDS (the stages are free now): each wave writes its 32 rows x 256 (bf16) or
+  // 128 (fp32) dims of the output into its own rows of 528 bytes (16 of padding keep the writes of
+  // the 32 rows of a column apart in the banks), then stores whole 512-byte row segments, 32 lanes
+  // x 16 bytes per row, instead of 16-byte pieces of 32 rows per store.
+  auto write_out = [&](auto bf) {
+    constexpr bool BF = decltype(bf)::value;
+    constexpr int kEs = BF ? 2 : 4;
+    constexpr int kGroup = BF ? 8 : 4;   // dim tiles per round
+    constexpr int kRowB = 528;
+    char* own = smem + w * 32 * kRowB;
 #pragma unroll
-    for (int dt = 0; dt < 16; ++dt) {
+    for (int g0 = 0; g0 < 16; g0 += kGroup) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        f32x4 v;
-        v[0] = o[dt][4 * q4 + 0];
-        v[1] = o[dt][4 * q4 + 1];
-        v[2] = o[dt][4 * q4 + 2];
-        v[3] = o[dt][4 * q4 + 3];
-        v *= inv;
-        const int64_t at = rowhead * kD + 32 * dt + 8 * q4 + 4 * half;
-        if (a.o_final_bf16) {
-          bf16x4 vb;
-          vb[0] = (bf16)v[0];
-          vb[1] = (bf16)v[1];
-          vb[2] = (bf16)v[2];
-          vb[3] = (bf16)v[3];
-          *(bf16x4*)((bf16*)a.o_final + at) = vb;
-        } else {
-          *(f32x4*)((float*)a.o_final + at) = v;
+      for (int dt = g0; dt < g0 + kGroup; ++dt) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          f32x4 v;
+          v[0] = o[dt][4 * q4 + 0];
+          v[1] = o[dt][4 * q4 + 1];
+          v[2] = o[dt][4 * q4 + 2];
+          v[3] = o[dt][4 * q4 + 3];
+          v *= inv;
+          char* at = own + n * kRowB + (32 * (dt - g0) + 8 * q4 + 4 * half) * kEs;
+          if constexpr (BF) {
+            bf16x4 vb;
+            vb[0] = (bf16)v[0];
+            vb[1] = (bf16)v[1];
+            vb[2] = (bf16)v[2];
+            vb[3] = (bf16)v[3];
+            *(bf16x4*)at = vb;
+          } else {
+            *(f32x4*)at = v;
+          }
+        }
+      }
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int r = 2 * it + half;   // the wave's row r: lanes 0..31 even rows, 32..63 odd
+        const int rho_r = 32 * w + r;
+        const int t = qb * QB + rho_r / G;
+        const u32x4 seg = *(const u32x4*)(own + r * kRowB + 16 * n);
+        if (t < a.T) {
+          const int64_t head = ((int64_t)b * a.T + t) * a.Hq + (int64_t)g * G + rho_r % G;
+          *(u32x4*)((char*)a.o_final + (head * kD + 32 * g0) * kEs + 16 * n) = seg;
         }
       }
     }
+  };
+  if (a.o_final_bf16)
+    write_out(std::true_type{});
+  else
+    write_out(std::false_type{});
+  if (row_valid) {
     if (half == 0) a.lse_final[rowhead] = nonempty ? (m_used + log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
