@@ -299,8 +299,8 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
       hook(p);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // the VALU reads the result next: wait out the last MFMA's passes
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    // the VALU reads the result next: the 12 wait states of an 8-pass MFMA's result
+    asm volatile("s_nop 7\n\ts_nop 3" ::: "memory");
     return acc;
   };
 
@@ -321,6 +321,7 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
   // value comes out exactly).  pass 0: the pass; 1: the reference follows every tile's maximum
   // (after a flag); 2: the pass again against the exact maxima.
   float m_used = -INFINITY, l_part = 0.0f, w_part = 0.0f;
+  bool need_ref = true;   // some row of the wave has no reference yet (wave-uniform)
   int pass = 0;
   f32x16 o[16];
 
@@ -359,7 +360,7 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
     }
     // the row maximum (a tree of 3-input maxima and the exchange with the row's other half), only
     // while some row of the wave has no reference yet, and in pass 1
-    if (pass == 1 || __ballot(m_used == -INFINITY) != 0) {
+    if (pass == 1 || need_ref) {
       float m6[6];
 #pragma unroll
       for (int k = 0; k < 5; ++k) m6[k] = fmaxf(fmaxf(sv[3 * k], sv[3 * k + 1]), sv[3 * k + 2]);
@@ -368,6 +369,7 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
       auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       mx = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1])) * scale_log2;
       m_used = (pass == 1 || m_used == -INFINITY) ? fmaxf(m_used, mx) : m_used;
+      need_ref = __ballot(m_used == -INFINITY) != 0;
     }
     neg_m = m_used == -INFINITY ? 0.0f : -m_used;
 #pragma unroll
