@@ -30,6 +30,8 @@
 //    with each row's reference following every tile's maximum (its exponents stay <= 0; its O is
 //    discarded), which leaves the exact row maxima, and once more in full against them.  O never
 //    leaves the registers before the end, and the pass needs no scratch memory.
+//  * At the end each wave stages its normalised O through the (then free) LDS stages and stores
+//    whole row segments.
 //  * Workgroups are launched latest query block first (longest causal work first).
 #include <type_traits>
 
@@ -111,7 +113,7 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
   constexpr int QB = 128 / G;  // query positions per workgroup
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
   __shared__ int s_lo[3][QB], s_hi[3][QB];
-  __shared__ int s_flag;   // some row's reference maximum must move
+  __shared__ int s_flag;   // some row's sums reached kSumMax: the workgroup reruns its sequence
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, n = l & 31, half = l >> 5;
