@@ -267,17 +267,13 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
   // wholly inside the cache, so the loads sit in the pairs' asm and take the precomputed lane
   // offsets; otherwise they follow the pairs in their general, clamped form); `hook(p)` runs
   // after pair p, inside its fence ---------------------------------------------------------------
-  auto scores = [&](auto inside, int stg_off, int dma_off, int dma_k0, auto&& hook) {
-    const char* raw = smem + stg_off + n * 1024;
-    const char* rot = smem + stg_off + kRawBytes + n * 256;
+  auto kld_at = [&](int stg_off, int s) {
+    if (s < 8) return *(const bf16x8*)(smem + stg_off + kRawBytes + n * 256 + qk_off[s]);
+    return *(const bf16x8*)(smem + stg_off + n * 1024 + 256 * (s >> 3) + qk_off[s & 7]);
+  };
+  auto scores = [&](auto inside, int stg_off, int dma_off, int dma_k0, auto&& hook, bf16x8* kf) {
     f32x16 acc;
-    bf16x8 kf[kDepthK];
-    auto kld = [&](int s) {
-      if (s < 8) return *(const bf16x8*)(rot + qk_off[s]);
-      return *(const bf16x8*)(raw + 256 * (s >> 3) + qk_off[s & 7]);
-    };
-#pragma unroll
-    for (int j = 0; j < kDepthK; ++j) kf[j] = kld(j);
+    auto kld = [&](int s) { return kld_at(stg_off, s); };
     const char* rawb = uniform_ptr((const char*)kraw_b + (int64_t)dma_k0 * raw_row);
     const char* rotb = uniform_ptr(krot_b + (int64_t)dma_k0 * rot_row);
     const uint32_t lds_d = __builtin_amdgcn_readfirstlane(smem_lds + dma_off);
@@ -323,6 +319,7 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
   // value comes out exactly).  pass 0: the pass; 1: the reference follows every tile's maximum
   // (after a flag); 2: the pass again against the exact maxima.
   float m_used = -INFINITY, l_part = 0.0f, w_part = 0.0f;
+  float neg_mu = 0.0f;   // -m_used, or 0 while the row has no reference (the exponents' bias)
   bool need_ref = true;   // some row of the wave has no reference yet (wave-uniform)
   int pass = 0;
   f32x16 o[16];
@@ -338,9 +335,10 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
     const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], scale_log2, neg_m));
     const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e + 1], scale_log2, neg_m));
     const bf16x2 pb = {(bf16)p0, (bf16)p1};
-    psum[(e >> 1) & 3] += p0 + p1;
-    wsum[(e >> 1) & 1] =
-        __builtin_amdgcn_fdot2_f32_bf16(pb, bf16x2{(bf16)1.0f, (bf16)1.0f}, wsum[(e >> 1) & 1], false);
+    // keys 0..7 of the tile start the partial sums (e < 8: psum[e/2]; e < 4: wsum[e/2])
+    psum[(e >> 1) & 3] = e < 8 ? p0 + p1 : psum[(e >> 1) & 3] + (p0 + p1);
+    wsum[(e >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(pb, bf16x2{(bf16)1.0f, (bf16)1.0f},
+                                                         e < 4 ? 0.0f : wsum[(e >> 1) & 1], false);
     pk[e >> 3][e & 7] = pb[0];
     pk[e >> 3][(e & 7) + 1] = pb[1];
   };
@@ -348,10 +346,9 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
   // The scores of tile i (raw, in sv): mask to each row's interval, reference of the row (the
   // first tile with a valid key sets it from its row maximum, O of the row being still 0), and the
   // probabilities of keys 0..15 of the tile (pk[0]).
-  auto softmax_head = [&](float* sv, int i, bf16x8* pk, float& neg_m, float* psum, float* wsum) {
+  auto softmax_head = [&](float* sv, int i, bool full, bf16x8* pk, float& neg_m, float* psum, float* wsum) {
     const int k0 = k0_of(i);
-    if (!(sel(i, full_lo[0], full_lo[1], full_lo[2]) <= k0 &&
-          k0 + kNK - 1 <= sel(i, full_hi[0], full_hi[1], full_hi[2]))) {
+    if (!full) {
       const int r = regime_of(i);
       const int lo_eff = s_lo[r][pos_in_blk] - k0, hi_eff = s_hi[r][pos_in_blk] - k0;
 #pragma unroll
@@ -371,12 +368,10 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
       auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       mx = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1])) * scale_log2;
       m_used = (pass == 1 || m_used == -INFINITY) ? fmaxf(m_used, mx) : m_used;
+      neg_mu = m_used == -INFINITY ? 0.0f : -m_used;
       need_ref = __ballot(m_used == -INFINITY) != 0;
     }
-    neg_m = m_used == -INFINITY ? 0.0f : -m_used;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) psum[k] = 0.0f;
-    wsum[0] = wsum[1] = 0.0f;
+    neg_m = neg_mu;
 #pragma unroll
     for (int e = 0; e < 8; e += 2) exp_pair(sv, e, neg_m, pk, psum, wsum);
   };
@@ -418,6 +413,11 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
       // tile i+2 was last read by the previous tile
       __builtin_amdgcn_s_waitcnt(0x0F70 | 10);   // vmcnt(10), expcnt and lgkmcnt open
       __syncthreads();
+      // the first K fragments go out first: the scalar work below runs in their LDS latency
+      bf16x8 kf[kDepthK];
+#pragma unroll
+      for (int j = 0; j < kDepthK; ++j) kf[j] = kld_at(off_c, j);
+      __builtin_amdgcn_sched_barrier(0);
       const int r = regime_of(i);
       if (r != cur_r) {
         // the compiler's wait counts do not see the tile loads in flight: settle everything so
@@ -429,6 +429,10 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
       // scores of tile i, with the loads of tile i+2 (past the end: the last tile again, into a
       // stage no longer read, which keeps ten loads per wave and tile in flight)
       const int dk0 = k0_of(min(i + 2, n_tiles - 1));
+      // the tile lies inside every row's interval (no masking)
+      const int k0i = k0_of(i);
+      const bool full = sel(i, full_lo[0], full_lo[1], full_lo[2]) <= k0i &&
+                        k0i + kNK - 1 <= sel(i, full_hi[0], full_hi[1], full_hi[2]);
       // the first V^T fragments of the tile go out with the last two score pairs (their LDS
       // latency then hides under those MFMAs and the softmax)
       bf16x8 vf[kDepthV];
@@ -439,14 +443,14 @@ __global__ __launch_bounds__(256, 1) void attn_fused_kernel(AttnArgs a, int n_qb
         }
         if (p == 15) vf[2] = vload(off_c, 2);
       };
-      const f32x16 acc = a.n_kv - 1 - dk0 >= kNK - 1 ? scores(std::true_type{}, off_c, off_d, dk0, hook)
-                                                     : scores(std::false_type{}, off_c, off_d, dk0, hook);
+      const f32x16 acc = a.n_kv - 1 - dk0 >= kNK - 1 ? scores(std::true_type{}, off_c, off_d, dk0, hook, kf)
+                                                     : scores(std::false_type{}, off_c, off_d, dk0, hook, kf);
       float sv[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) sv[e] = acc[e];
       bf16x8 pk[2];
       float neg_m, psum[4], wsum[2];
-      softmax_head(sv, i, pk, neg_m, psum, wsum);
+      softmax_head(sv, i, full, pk, neg_m, psum, wsum);
       // O^T of tile i; the probabilities of keys 16..31 (pk[1], first used by MFMA 16) are formed
       // after MFMAs 1, 4, 7, 10
       values(off_c, pk, [&](int j) {
