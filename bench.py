@@ -268,8 +268,9 @@ def main():
                     help="also run one plain 1 GiB device copy (reference for the traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this path has no multi-GPU mode (see DESIGN.md for how it "
-              "would shard); run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: this path has no multi-GPU mode (a layer would shard by KV "
+              "head, one or more of the 2 per GPU, or split the key cache across GPUs and merge the "
+              "partials by their LSE); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
