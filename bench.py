@@ -177,7 +177,7 @@ def cpu_baseline(w, inp, n_rows, seed=0):
 
 
 def measured_peaks(torch, dca):
-    """On-box reference rates from the library's probe kernels (include/dca_calibrate.h): bf16
+    """Reference rates measured on the device from the library's probe kernels (include/dca_calibrate.h): bf16
     MFMA 32x32x16 with no memory traffic (2048 workgroups of 4 waves), and a streaming read of
     4 GiB with 16-byte loads (8192 workgroups)."""
     def timed(fn, reps):

@@ -1,6 +1,6 @@
-// On-box reference rates for the roofline fractions the benchmark reports next to the vendor
-// peaks: a matrix-core loop with no memory traffic (bf16 MFMA 32x32x16, the instruction of the
-// prefill passes) and a streaming read of a device buffer (the access of the decode pass).
+// Reference rates measured on the device for the roofline fractions the benchmark reports next to
+// the vendor peaks: a matrix-core loop with no memory traffic (bf16 MFMA 32x32x16, the instruction
+// of the prefill passes) and a streaming read of a device buffer (the access of the decode pass).
 // Neither is part of the attention path.
 #include "common.h"
 
@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int32_t iters, float* _
 }
 
 // 16-byte nontemporal loads, eight in flight per thread per step, grid-stride over n16 = bytes / 16
-// (of the forms tried on the box: four or eight in flight, with or without the nontemporal hint,
+// (of the forms tried on MI355X: four or eight in flight, with or without the nontemporal hint,
 // 2048 to 32768 workgroups, this one read fastest)
 __global__ __launch_bounds__(256) void probe_read_kernel(const uint4* __restrict__ src, int64_t n16,
                                                          float* __restrict__ sink) {

@@ -1,4 +1,4 @@
-/* On-box reference rates for roofline fractions (not part of the attention path).
+/* Reference rates measured on the device for roofline fractions (not part of the attention path).
  *
  * The attention kernels' achieved rates are reported against the vendor peaks and against what
  * the same GPU reaches on the simplest kernel of each kind; these two entry points are those
